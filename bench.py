@@ -1,0 +1,170 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed MoE layer on one MI355X.
+
+A step is one moe_forward call -- routing plan, gather, grouped expert FFN and
+combine -- over the prefill workload: T=2048 tokens, hidden 2560, 512 experts,
+top-10, expert FFN 768, fp16 activations and weights, tm=16, seeded synthetic
+routing (router logits N(0,1)). Inputs and weights are resident in HBM before
+the timed region. Prints one JSON line.
+
+The roofline object covers the dominant kernel (the gate/up + SwiGLU grouped
+GEMM), bound by HBM: algorithmic bytes per launch (weights of the experts the
+plan touches, gathered rows read, SwiGLU output written) divided by its
+average launch time, measured with HIP events recorded by the library around
+that kernel on its stream during the timed steps.
+
+cpu_baseline: the CPU oracle (plain C, fp64, OpenMP over tokens) timed on the
+host cores on a bounded sample of the same workload: the plan over all 2048
+tokens plus gather and naive expert FFN for a prefix of the tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed (token,expert) rows/sec per MoE layer, T=2048 E=512 top-10; plan us/layer"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_fp16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock target of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def gateup_bytes(cfg, meta):
+    """Algorithmic HBM bytes of one gate/up launch: both weight matrices of every
+    expert that has rows, the gathered rows read once, the SwiGLU output written."""
+    es = 2 if cfg.dtype != "f32" else 4
+    nactive, nr = int(meta[4]), int(meta[2])
+    return 2 * nactive * cfg.d * cfg.f * es + nr * cfg.d * es + nr * cfg.f * es
+
+
+def cpu_baseline(cfg, ids, w, x, seconds):
+    import oracle
+    from mixture_experts_routed_amd import synth
+
+    nth = oracle.nthreads_default()
+    # weights on the host (regenerated from the same seeds)
+    t0 = time.perf_counter()
+    Wg, Wu, Wd = (synth.expert_weights(cfg, k) for k in ("gate", "up", "down"))
+    log(f"cpu_baseline: host weights in {time.perf_counter() - t0:.1f}s, {nth} threads")
+
+    def run(ntok):
+        t = time.perf_counter()
+        p = oracle.plan(ids, w, cfg.E, cfg.tm)
+        sel = np.arange(ntok, dtype=np.int32)
+        used = np.isin(p["stok"], sel)
+        oracle.gather(x, np.where(used, p["stok"], -1).astype(np.int32))
+        oracle.ffn(x, ids, w, Wg, Wu, Wd, cfg.dtype, True, tokens=sel, nthreads=nth)
+        return time.perf_counter() - t
+
+    probe = max(nth, 8)
+    tp = run(probe)
+    ntok = int(min(cfg.T, max(probe, round(probe * seconds / max(tp, 1e-3)))))
+    ntok = max(nth, ntok // nth * nth)
+    tt = run(ntok)
+    rows = ntok * cfg.K
+    return {"value": rows / tt, "unit": "rows/s", "cores": nth, "kind": "oracle",
+            "sample": f"plan of all {cfg.T} tokens + gather + naive fp64 expert FFN of the first "
+                      f"{ntok} tokens ({rows} routed rows), {tt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the layer is measured at one GPU's share; see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_routed_amd import abi, synth
+
+    cfg = synth.CONFIGS[args.workload]
+    assert cfg.chunk == 0 or cfg.chunk == cfg.T, "bench workload must be a single layer call"
+    T, K, E, d, f, tm = cfg.T, cfg.K, cfg.E, cfg.d, cfg.f, cfg.tm
+    t0 = time.perf_counter()
+    ids, w = synth.routing(cfg)
+    x = synth.activations(cfg)
+    tdt = abi.TORCH_DTYPE[abi.DTYPE_NAME[cfg.dtype]]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        t = t.to("cuda")
+        return t.view(tdt) if a.dtype == np.uint16 else t
+
+    dev = torch.device("cuda:0")
+    wts = {k: up(synth.expert_weights(cfg, k)) for k in ("gate", "up", "down")}
+    xd, idsd, wd = up(x), torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+
+    ws = torch.empty(abi.moe_forward_workspace(T, K, E, d, f, tm, abi.DTYPE_NAME[cfg.dtype]),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    timer = abi.Timer(capacity=max(args.steps, 1))
+
+    def step(tmr=None):
+        abi.forward(xd, idsd, wd, wts["gate"], wts["up"], wts["down"], tm=tm, workspace=ws, out=out,
+                    timer=tmr)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    st = timer.read()
+    timer.close()
+
+    L = abi.moe_forward_layout(T, K, E, d, f, tm, abi.DTYPE_NAME[cfg.dtype])
+    meta = ws[L.meta: L.meta + 4 * abi.META_N].view(torch.int32).cpu().numpy()
+    us = {k: 1e3 * v[0] / max(v[1], 1) for k, v in st.items()}
+    gu_bytes = gateup_bytes(cfg, meta)
+    gu_s = us["gateup"] * 1e-6
+    achieved = gu_bytes / gu_s / 1e9
+    rows = T * K
+    res = {
+        "metric": METRIC, "value": rows / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d": d, "E": E, "top_k": K, "f": f, "tm": tm,
+                   "routing": "router logits N(0,1), softmax top-k renormalised"},
+        "plan_us": us["hist"] + us["scan"] + us["place"],
+        "stages_us": {k: round(v, 2) for k, v in us.items()},
+        "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
+        "roofline": {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": gu_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

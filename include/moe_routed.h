@@ -1,0 +1,253 @@
+/*
+ * moe_routed.h -- C ABI of the routed mixture-of-experts layer for AMD
+ * Instinct MI355X (gfx950): routing plan, activation gather, grouped expert
+ * FFN (gate/up projection + SwiGLU, weighted down projection) and a
+ * fixed-order combine.
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *  [P1] "Round 4 Track C: Prefill MoE Plan (mm_clear + mm_hist + mm_scan +
+ *       mm_place) & Epilogue / Gather Audit" -- s.1 findings 1-4, s.2
+ *       Table 2.1, s.3 Bitwise & Numerical Parity.
+ *  [P3] "Batched resident MoE experts on Apple Silicon: a flat parallel expert
+ *       pass" -- s.1 Contribution (job list of (token, expert, weight);
+ *       gate/up -> gated activation -> weighted down projection), s.3
+ *       Results (fixed per-token top-k summation order).
+ *  [P4] "Add --moe-mode sweep-prefill: streamed expert supply for CPU
+ *       mul_mat_id" -- Mechanism (experts in ascending id order over
+ *       contiguous slices).
+ *
+ * Common conventions
+ *  - Entry i = t*K + k: token t's k-th routed expert (token-major), k in the
+ *    router's order.
+ *  - Element types (enum moe_dtype): activations x, gathered rows xs, expert
+ *    weights and the SwiGLU output h share one type D. Accumulation is fp32.
+ *    Router weights w, the per-row weight sw, expert outputs y and the layer
+ *    output are fp32.
+ *  - Weight layouts, row-major: w_gate and w_up [E][d][f] (input index, then
+ *    output index), w_down [E][f][d].
+ *  - Pointers: every array argument is a DEVICE pointer (hipMalloc'd or
+ *    equivalent), owned by the caller. The library allocates and frees no
+ *    device memory and keeps no state between calls. Arrays must not alias,
+ *    except that a scratch/workspace buffer may be reused by later calls on
+ *    the same stream. Structs passed by pointer (sizes, timers) live on the
+ *    host.
+ *  - Streams: every call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *    is the default stream) and returns without waiting. Data-dependent
+ *    scalars (row counts) stay on the device in `meta` and are read there by
+ *    later calls.
+ *  - Outputs need no clearing: every element a call defines is written on
+ *    every call.
+ *  - Errors: each call returns MOE_OK or an error code; nothing prints, throws
+ *    or aborts. MOE_EINVAL: a NULL or misaligned pointer (data arrays need
+ *    16-byte alignment, index arrays 4-byte), a size out of range, an
+ *    undersized scratch or workspace. MOE_EUNSUPPORTED: a valid request this
+ *    build does not implement (E > MOE_MAX_EXPERTS). MOE_EHIP: the HIP
+ *    runtime refused a launch (e.g. no device). Argument checks happen before
+ *    any HIP call.
+ *  - Ids: -1 marks a skipped entry ([P1] s.3: experts skipped by tail
+ *    skipping); it gets no row and pos = -1. Any other id outside [0, E) is
+ *    counted in meta[MOE_META_NBAD] and treated the same way.
+ *  - Inconsistent plan arrays passed to the later calls (made up rather than
+ *    produced by moe_plan) give unspecified values but never an access
+ *    outside the stated array sizes: row and token indices are clamped to
+ *    their bounds on the device.
+ */
+#ifndef MOE_ROUTED_H
+#define MOE_ROUTED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moe_stream_t; /* hipStream_t */
+
+enum moe_dtype { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2 };
+
+enum moe_status { MOE_OK = 0, MOE_EINVAL = 1, MOE_EUNSUPPORTED = 2, MOE_EHIP = 3 };
+
+/* Fields of the device array meta[MOE_META_N] written by moe_plan. */
+enum moe_meta_field {
+    MOE_META_NENT = 0,    /* T*K entries */
+    MOE_META_NBLK = 1,    /* plan blocks of MOE_PLAN_BLOCK entries */
+    MOE_META_NR = 2,      /* rows of the expert-sorted list, pads included */
+    MOE_META_NT = 3,      /* tiles of tm rows: nr / tm */
+    MOE_META_NACTIVE = 4, /* experts with at least one entry */
+    MOE_META_MAXCNT = 5,  /* largest entry count of one expert */
+    MOE_META_NSKIP = 6,   /* entries with id -1 */
+    MOE_META_NBAD = 7,    /* entries with another id outside [0, E) */
+    MOE_META_TM = 8,
+    MOE_META_E = 9,
+    MOE_META_K = 10,
+    MOE_META_N = 11
+};
+
+#define MOE_MAX_EXPERTS 1024 /* one plan counter per expert in LDS ([P1] s.1 finding 1: 1024 counters) */
+#define MOE_PLAN_BLOCK 1024  /* entries per plan block (the page's block size) */
+
+/* Host-side sizes of a plan. */
+typedef struct {
+    int64_t nent;         /* T*K */
+    int64_t nblk;         /* ceil(nent / MOE_PLAN_BLOCK) */
+    int64_t max_rows;     /* upper bound of nr: rows to allocate for stok, sw, xs, h, y */
+    int64_t max_tiles;    /* max_rows / tm */
+    size_t scratch_bytes; /* device scratch moe_plan needs */
+} moe_plan_sizes_t;
+
+/*
+ * moe_plan_sizes -- host only, no HIP call.
+ * max_rows = ceil((T*K + min(E, T*K)*(tm-1)) / tm) * tm: every valid entry has
+ * a row and each active expert adds at most tm-1 pad rows.
+ * Returns MOE_EINVAL if T, K, E or tm < 1, T*K >= 2^31 or max_rows >= 2^31;
+ * MOE_EUNSUPPORTED if E > MOE_MAX_EXPERTS.
+ */
+int moe_plan_sizes(int T, int K, int E, int tm, moe_plan_sizes_t *out);
+
+/*
+ * moe_plan -- the routing plan ([P1] s.1 findings 1 and 2; s.3 lists the
+ * outputs): a per-block expert histogram, a prefix scan of the per-expert
+ * counts padded up to a multiple of tm (pad rows marked -1 in the same pass),
+ * and a placement of every entry into an expert-sorted row list. Experts are
+ * laid out in ascending id order ([P4] Mechanism). Inside one expert the rows
+ * follow entry order (stable by token, then k), so the plan is unique.
+ *
+ * In:  ids [T*K] int32, w [T*K] fp32 (router weight of each entry).
+ * Out: cnt [E]            entries per expert
+ *      eoff [E+1]         first row of each expert; eoff[E] = nr
+ *      tiles [max_tiles]  expert of each tm-row tile, tiles [0, nt) written
+ *      stok [max_rows]    token of each row; -1 on pad rows; rows [0, nr) written
+ *      sw [max_rows]      router weight of each row (bit copy of w); +0.0 on pad rows
+ *      pos [T*K]          row of each entry; -1 for skipped/bad entries
+ *      boff [nblk*E]      entries of expert e in the blocks before block b, at [b*E + e]
+ *      meta [MOE_META_N]  see enum moe_meta_field
+ * scratch: device buffer of at least moe_plan_sizes().scratch_bytes.
+ * Errors: as moe_plan_sizes, plus MOE_EINVAL for NULL/misaligned pointers or
+ * a small scratch; MOE_EHIP on a failed launch.
+ */
+int moe_plan(const int32_t *ids, const float *w, int T, int K, int E, int tm, int32_t *cnt,
+             int32_t *eoff, int32_t *tiles, int32_t *stok, float *sw, int32_t *pos, int32_t *boff,
+             int32_t *meta, void *scratch, size_t scratch_bytes, moe_stream_t stream);
+
+/*
+ * moe_gather -- [P1] s.1 finding 4: copy each routed token's row of the
+ * half-precision activation into expert-contiguous rows, bit for bit.
+ * xs[r][:] = x[stok[r]][:] for r < min(meta[MOE_META_NR], max_rows); pad rows
+ * (stok[r] < 0) become all-zero bits. Rows >= nr are not touched.
+ * In:  x [T][d] of dtype, stok [max_rows], meta [MOE_META_N] (device, from moe_plan).
+ * Out: xs [max_rows][d] of dtype.
+ * Errors: MOE_EINVAL for d < 8 or d % 8 != 0, T < 1, max_rows < 1, bad dtype,
+ * NULL/misaligned pointers; MOE_EHIP on a failed launch.
+ */
+int moe_gather(const void *x, int dtype, int T, int d, const int32_t *stok, const int32_t *meta,
+               int64_t max_rows, void *xs, moe_stream_t stream);
+
+/*
+ * moe_ffn_scratch_bytes -- host only: scratch moe_expert_ffn needs for a plan
+ * of at most max_rows rows over E experts with tile tm.
+ */
+int moe_ffn_scratch_bytes(int E, int tm, int64_t max_rows, size_t *bytes);
+
+/*
+ * moe_expert_ffn -- the grouped expert FFN over the expert-sorted rows
+ * ([P3] s.1: gate/up projection, gated activation, weighted down projection
+ * per job; [P1] s.1 finding 5 names the SwiGLU and down-projection epilogue
+ * kernels). For every row r in expert e's range [eoff[e], eoff[e+1]):
+ *   g = xs[r] . w_gate[e],  u = xs[r] . w_up[e]            (fp32 accumulation)
+ *   h[r][j] = D( silu(g[j]) * u[j] ),  silu(z) = z / (1 + exp(-z))
+ *   y[r][c] = sw[r] * sum_j h[r][j] * w_down[e][j][c]      (fp32)
+ * h is stored in D (the operand type of the down projection, like the page's
+ * half SwiGLU output) for every row of every expert range; y is stored only
+ * on rows with stok[r] >= 0 (pad rows are never read by moe_combine).
+ * In:  xs [max_rows][d], w_gate/w_up [E][d][f], w_down [E][f][d] (dtype),
+ *      eoff [E+1], stok [max_rows], sw [max_rows], meta [MOE_META_N].
+ * Out: h [max_rows][f] (dtype), y [max_rows][d] fp32.
+ * scratch: at least moe_ffn_scratch_bytes().
+ * Errors: MOE_EINVAL for d or f not positive multiples of 8, bad dtype,
+ * NULL/misaligned pointers, small scratch, tm < 1; MOE_EUNSUPPORTED for
+ * E > MOE_MAX_EXPERTS; MOE_EHIP on a failed launch.
+ */
+int moe_expert_ffn(const void *xs, const void *w_gate, const void *w_up, const void *w_down,
+                   int dtype, int E, int d, int f, int tm, const int32_t *eoff, const int32_t *stok,
+                   const float *sw, const int32_t *meta, int64_t max_rows, void *h, float *y,
+                   void *scratch, size_t scratch_bytes, moe_stream_t stream);
+
+/*
+ * moe_combine -- sum each token's expert outputs in the fixed top-k order
+ * ([P3] s.3: the same per-token top-k summation order gives bit-identical
+ * results): out[t][c] = +0.0f, then += y[pos[t*K+k]][c] for k = 0..K-1 in fp32,
+ * skipping pos < 0 (and pos >= max_rows). One correct fp32 result exists for
+ * this order, and this call produces it.
+ * In:  y [max_rows][d] fp32, pos [T*K]. Out: out [T][d] fp32.
+ * Errors: MOE_EINVAL for d % 8 != 0, T/K < 1, NULL/misaligned pointers;
+ * MOE_EHIP on a failed launch.
+ */
+int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,
+                float *out, moe_stream_t stream);
+
+/*
+ * moe_forward_workspace -- host only: bytes of the workspace moe_forward
+ * carves its intermediates from (plan arrays, xs, h, y, scratch).
+ */
+int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, size_t *bytes);
+
+/*
+ * moe_forward -- one routed MoE layer: moe_plan, moe_gather, moe_expert_ffn
+ * and moe_combine in sequence on one stream, intermediates in `workspace`.
+ * In:  x [T][d] (dtype), ids [T*K], w [T*K], expert weights as above.
+ * Out: out [T][d] fp32.
+ * Errors: the union of the four calls' errors.
+ */
+int moe_forward(const void *x, const int32_t *ids, const float *w, const void *w_gate,
+                const void *w_up, const void *w_down, int dtype, int T, int K, int E, int d, int f,
+                int tm, void *workspace, size_t ws_bytes, float *out, moe_stream_t stream);
+
+/* Byte offsets of moe_forward's intermediates inside the workspace (host only),
+ * so that a caller can inspect them after a call. */
+typedef struct {
+    size_t cnt, eoff, tiles, stok, sw, pos, boff, meta, plan_scratch, xs, h, y, ffn_scratch, total;
+} moe_forward_layout_t;
+int moe_forward_layout(int T, int K, int E, int d, int f, int tm, int dtype,
+                       moe_forward_layout_t *out);
+
+/* ---- per-kernel timing (HIP events recorded around each kernel) ---- */
+
+enum moe_stage {
+    MOE_STAGE_HIST = 0,
+    MOE_STAGE_SCAN,
+    MOE_STAGE_PLACE,
+    MOE_STAGE_GATHER,
+    MOE_STAGE_WORKLIST,
+    MOE_STAGE_GATEUP,
+    MOE_STAGE_DOWN,
+    MOE_STAGE_COMBINE,
+    MOE_STAGE_N
+};
+
+typedef struct moe_timer moe_timer_t;
+
+/* Create a timer that can hold `capacity` recorded calls (host object; its
+ * HIP events are created on the current device). */
+int moe_timer_create(moe_timer_t **out, int capacity);
+int moe_timer_destroy(moe_timer_t *timer);
+/* Wait for the recorded events, add each stage's elapsed milliseconds into
+ * total_ms[MOE_STAGE_N] and its launch count into launches[MOE_STAGE_N], then
+ * forget the recorded calls. */
+int moe_timer_read(moe_timer_t *timer, double *total_ms, int64_t *launches);
+
+/* moe_forward with an event pair recorded around every kernel into `timer`
+ * (NULL: identical to moe_forward). MOE_EINVAL when the timer is full. */
+int moe_forward_timed(const void *x, const int32_t *ids, const float *w, const void *w_gate,
+                      const void *w_up, const void *w_down, int dtype, int T, int K, int E, int d,
+                      int f, int tm, void *workspace, size_t ws_bytes, float *out,
+                      moe_stream_t stream, moe_timer_t *timer);
+
+/* Static description of a status code. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTED_H */

@@ -1,0 +1,397 @@
+// C ABI of the routed MoE layer (declared in include/moe_routed.h): argument
+// checks on the host, then kernel launches on the caller's stream. No device
+// allocation, no host synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "../../include/moe_routed.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+bool dtype_ok(int dtype) { return dtype == MOE_F32 || dtype == MOE_F16 || dtype == MOE_BF16; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+hipStream_t as_stream(moe_stream_t s) { return static_cast<hipStream_t>(s); }
+
+int plan_sizes(int T, int K, int E, int tm, moe_plan_sizes_t *o)
+{
+    if (T < 1 || K < 1 || E < 1 || tm < 1) return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    const int64_t nent = (int64_t)T * K;
+    if (nent > kI32Max - MOE_PLAN_BLOCK) return MOE_EINVAL;
+    const int64_t act = nent < E ? nent : E;
+    const int64_t rows = (nent + act * (tm - 1) + tm - 1) / tm * tm;
+    if (rows > kI32Max - 1024) return MOE_EINVAL;
+    o->nent = nent;
+    o->nblk = (nent + MOE_PLAN_BLOCK - 1) / MOE_PLAN_BLOCK;
+    o->max_rows = rows;
+    o->max_tiles = rows / tm;
+    o->scratch_bytes = (size_t)o->nblk * (size_t)(E + 2) * sizeof(int32_t);
+    return MOE_OK;
+}
+
+int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, int dtype, int E,
+              int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
+              const int32_t *meta, int64_t max_rows, const void *h, const float *y,
+              const void *scratch, size_t scratch_bytes)
+{
+    if (!dtype_ok(dtype) || E < 1 || tm < 1 || d < 8 || f < 8 || d % 8 || f % 8 || max_rows < 1 ||
+        max_rows > kI32Max - 1024)
+        return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    if (max_rows * (int64_t)(d > f ? d : f) > ((int64_t)1 << 40)) return MOE_EINVAL;
+    if (!aligned(xs, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) ||
+        !aligned(h, 16) || !aligned(y, 16) || !aligned(eoff, 4) || !aligned(stok, 4) ||
+        !aligned(sw, 4) || !aligned(meta, 4) || !aligned(scratch, 16))
+        return MOE_EINVAL;
+    if (scratch_bytes < moe::ffn_scratch_bytes(E, tm, max_rows)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+// Record an event pair around each kernel when a timer is attached.
+}  // namespace
+
+struct moe_timer {
+    int capacity;
+    int used[MOE_STAGE_N];
+    hipEvent_t *ev[MOE_STAGE_N];  // 2 * capacity events per stage
+};
+
+namespace {
+
+struct Rec {
+    moe_timer_t *t;
+    hipStream_t s;
+    int stage;
+    bool on;
+    Rec(moe_timer_t *t_, hipStream_t s_, int stage_) : t(t_), s(s_), stage(stage_), on(false)
+    {
+        if (t && t->used[stage] < t->capacity) {
+            (void)hipEventRecord(t->ev[stage][2 * t->used[stage]], s);
+            on = true;
+        }
+    }
+    ~Rec()
+    {
+        if (on) {
+            (void)hipEventRecord(t->ev[stage][2 * t->used[stage] + 1], s);
+            t->used[stage]++;
+        }
+    }
+};
+
+bool timer_room(const moe_timer_t *t)
+{
+    if (!t) return true;
+    for (int q = 0; q < MOE_STAGE_N; ++q)
+        if (t->used[q] >= t->capacity) return false;
+    return true;
+}
+
+int plan_impl(const int32_t *ids, const float *w, int T, int K, int E, int tm, int32_t *cnt,
+              int32_t *eoff, int32_t *tiles, int32_t *stok, float *sw, int32_t *pos, int32_t *boff,
+              int32_t *meta, void *scratch, size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr)
+{
+    moe_plan_sizes_t z;
+    const int rc = plan_sizes(T, K, E, tm, &z);
+    if (rc != MOE_OK) return rc;
+    if (!aligned(ids, 4) || !aligned(w, 4) || !aligned(cnt, 4) || !aligned(eoff, 4) ||
+        !aligned(tiles, 4) || !aligned(stok, 4) || !aligned(sw, 4) || !aligned(pos, 4) ||
+        !aligned(boff, 4) || !aligned(meta, 4) || !aligned(scratch, 4) ||
+        scratch_bytes < z.scratch_bytes)
+        return MOE_EINVAL;
+    const int nent = (int)z.nent, nblk = (int)z.nblk;
+    int32_t *bcnt = static_cast<int32_t *>(scratch);
+    {
+        Rec r(tmr, s, MOE_STAGE_HIST);
+        if (moe::launch_hist(ids, nent, E, nblk, bcnt, s) != hipSuccess) return MOE_EHIP;
+    }
+    {
+        Rec r(tmr, s, MOE_STAGE_SCAN);
+        if (moe::launch_scan(bcnt, nblk, E, K, tm, nent, cnt, eoff, boff, tiles, stok, sw, meta,
+                             s) != hipSuccess)
+            return MOE_EHIP;
+    }
+    {
+        Rec r(tmr, s, MOE_STAGE_PLACE);
+        if (moe::launch_place(ids, w, nent, E, K, nblk, eoff, boff, stok, sw, pos, s) != hipSuccess)
+            return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int gather_impl(const void *x, int dtype, int T, int d, const int32_t *stok, const int32_t *meta,
+                int64_t max_rows, void *xs, hipStream_t s, moe_timer_t *tmr)
+{
+    if (!dtype_ok(dtype) || T < 1 || d < 8 || d % 8 || max_rows < 1 || max_rows > kI32Max)
+        return MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(xs, 16) || !aligned(stok, 4) || !aligned(meta, 4))
+        return MOE_EINVAL;
+    Rec r(tmr, s, MOE_STAGE_GATHER);
+    if (moe::launch_gather(x, elem_bytes(dtype), T, d, stok, meta, max_rows, xs, s) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int dtype, int E,
+             int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
+             const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
+             size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr)
+{
+    const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
+                             y, scratch, scratch_bytes);
+    if (rc != MOE_OK) return rc;
+    const int64_t max_items = moe::ffn_max_items(E, tm, max_rows);
+    {
+        Rec r(tmr, s, MOE_STAGE_WORKLIST);
+        if (moe::launch_worklist(eoff, E, max_rows, scratch, max_items, s) != hipSuccess)
+            return MOE_EHIP;
+    }
+    {
+        Rec r(tmr, s, MOE_STAGE_GATEUP);
+        if (moe::launch_gateup(dtype, xs, wg, wu, d, f, scratch, max_items, h, s) != hipSuccess)
+            return MOE_EHIP;
+    }
+    {
+        Rec r(tmr, s, MOE_STAGE_DOWN);
+        if (moe::launch_down(dtype, h, wd, d, f, stok, sw, scratch, max_items, y, s) != hipSuccess)
+            return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int combine_impl(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,
+                 float *out, hipStream_t s, moe_timer_t *tmr)
+{
+    if (T < 1 || K < 1 || d < 8 || d % 8 || max_rows < 1 || (int64_t)T * K > kI32Max)
+        return MOE_EINVAL;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(pos, 4)) return MOE_EINVAL;
+    Rec r(tmr, s, MOE_STAGE_COMBINE);
+    if (moe::launch_combine(y, max_rows, pos, T, K, d, out, s) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+}
+
+int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forward_layout_t *L,
+                moe_plan_sizes_t *z)
+{
+    if (!L || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 || f % 8) return MOE_EINVAL;
+    const int rc = plan_sizes(T, K, E, tm, z);
+    if (rc != MOE_OK) return rc;
+    const size_t A = 256, es = (size_t)elem_bytes(dtype), R = (size_t)z->max_rows;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = round_up(o + bytes, A);
+        return at;
+    };
+    L->cnt = take((size_t)E * 4);
+    L->eoff = take((size_t)(E + 1) * 4);
+    L->tiles = take((size_t)z->max_tiles * 4);
+    L->stok = take(R * 4);
+    L->sw = take(R * 4);
+    L->pos = take((size_t)z->nent * 4);
+    L->boff = take((size_t)z->nblk * E * 4);
+    L->meta = take(MOE_META_N * 4);
+    L->plan_scratch = take(z->scratch_bytes);
+    L->xs = take(R * d * es);
+    L->h = take(R * f * es);
+    L->y = take(R * d * 4);
+    L->ffn_scratch = take(moe::ffn_scratch_bytes(E, tm, z->max_rows));
+    L->total = o;
+    return MOE_OK;
+}
+
+int forward_impl(const void *x, const int32_t *ids, const float *w, const void *wg, const void *wu,
+                 const void *wd, int dtype, int T, int K, int E, int d, int f, int tm, void *ws,
+                 size_t ws_bytes, float *out, hipStream_t s, moe_timer_t *tmr)
+{
+    moe_forward_layout_t L;
+    moe_plan_sizes_t z;
+    int rc = layout_impl(T, K, E, d, f, tm, dtype, &L, &z);
+    if (rc != MOE_OK) return rc;
+    if (!aligned(ws, 256) || ws_bytes < L.total || !aligned(x, 16) || !aligned(out, 16) ||
+        !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16))
+        return MOE_EINVAL;
+    if (!timer_room(tmr)) return MOE_EINVAL;
+    char *b = static_cast<char *>(ws);
+    auto i32 = [&](size_t off) { return reinterpret_cast<int32_t *>(b + off); };
+    auto f32 = [&](size_t off) { return reinterpret_cast<float *>(b + off); };
+    rc = plan_impl(ids, w, T, K, E, tm, i32(L.cnt), i32(L.eoff), i32(L.tiles), i32(L.stok),
+                   f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
+                   z.scratch_bytes, s, tmr);
+    if (rc != MOE_OK) return rc;
+    rc = gather_impl(x, dtype, T, d, i32(L.stok), i32(L.meta), z.max_rows, b + L.xs, s, tmr);
+    if (rc != MOE_OK) return rc;
+    rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
+                  i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
+                  moe::ffn_scratch_bytes(E, tm, z.max_rows), s, tmr);
+    if (rc != MOE_OK) return rc;
+    return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_plan_sizes(int T, int K, int E, int tm, moe_plan_sizes_t *out)
+{
+    if (!out) return MOE_EINVAL;
+    return plan_sizes(T, K, E, tm, out);
+}
+
+int moe_plan(const int32_t *ids, const float *w, int T, int K, int E, int tm, int32_t *cnt,
+             int32_t *eoff, int32_t *tiles, int32_t *stok, float *sw, int32_t *pos, int32_t *boff,
+             int32_t *meta, void *scratch, size_t scratch_bytes, moe_stream_t stream)
+{
+    return plan_impl(ids, w, T, K, E, tm, cnt, eoff, tiles, stok, sw, pos, boff, meta, scratch,
+                     scratch_bytes, as_stream(stream), nullptr);
+}
+
+int moe_gather(const void *x, int dtype, int T, int d, const int32_t *stok, const int32_t *meta,
+               int64_t max_rows, void *xs, moe_stream_t stream)
+{
+    return gather_impl(x, dtype, T, d, stok, meta, max_rows, xs, as_stream(stream), nullptr);
+}
+
+int moe_ffn_scratch_bytes(int E, int tm, int64_t max_rows, size_t *bytes)
+{
+    if (!bytes || E < 1 || tm < 1 || max_rows < 1 || max_rows > kI32Max - 1024) return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    *bytes = moe::ffn_scratch_bytes(E, tm, max_rows);
+    return MOE_OK;
+}
+
+int moe_expert_ffn(const void *xs, const void *w_gate, const void *w_up, const void *w_down,
+                   int dtype, int E, int d, int f, int tm, const int32_t *eoff, const int32_t *stok,
+                   const float *sw, const int32_t *meta, int64_t max_rows, void *h, float *y,
+                   void *scratch, size_t scratch_bytes, moe_stream_t stream)
+{
+    return ffn_impl(xs, w_gate, w_up, w_down, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
+                    y, scratch, scratch_bytes, as_stream(stream), nullptr);
+}
+
+int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,
+                float *out, moe_stream_t stream)
+{
+    return combine_impl(y, max_rows, pos, T, K, d, out, as_stream(stream), nullptr);
+}
+
+int moe_forward_layout(int T, int K, int E, int d, int f, int tm, int dtype,
+                       moe_forward_layout_t *out)
+{
+    moe_plan_sizes_t z;
+    return layout_impl(T, K, E, d, f, tm, dtype, out, &z);
+}
+
+int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, size_t *bytes)
+{
+    if (!bytes) return MOE_EINVAL;
+    moe_forward_layout_t L;
+    moe_plan_sizes_t z;
+    const int rc = layout_impl(T, K, E, d, f, tm, dtype, &L, &z);
+    if (rc == MOE_OK) *bytes = L.total;
+    return rc;
+}
+
+int moe_forward(const void *x, const int32_t *ids, const float *w, const void *w_gate,
+                const void *w_up, const void *w_down, int dtype, int T, int K, int E, int d, int f,
+                int tm, void *workspace, size_t ws_bytes, float *out, moe_stream_t stream)
+{
+    return forward_impl(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace,
+                        ws_bytes, out, as_stream(stream), nullptr);
+}
+
+int moe_forward_timed(const void *x, const int32_t *ids, const float *w, const void *w_gate,
+                      const void *w_up, const void *w_down, int dtype, int T, int K, int E, int d,
+                      int f, int tm, void *workspace, size_t ws_bytes, float *out,
+                      moe_stream_t stream, moe_timer_t *timer)
+{
+    return forward_impl(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace,
+                        ws_bytes, out, as_stream(stream), timer);
+}
+
+int moe_timer_create(moe_timer_t **out, int capacity)
+{
+    if (!out || capacity < 1 || capacity > (1 << 20)) return MOE_EINVAL;
+    moe_timer_t *t = new (std::nothrow) moe_timer_t();
+    if (!t) return MOE_EINVAL;
+    t->capacity = capacity;
+    for (int q = 0; q < MOE_STAGE_N; ++q) {
+        t->used[q] = 0;
+        t->ev[q] = nullptr;
+    }
+    for (int q = 0; q < MOE_STAGE_N; ++q) {
+        t->ev[q] = new (std::nothrow) hipEvent_t[2 * (size_t)capacity]();
+        if (!t->ev[q]) {
+            moe_timer_destroy(t);
+            return MOE_EINVAL;
+        }
+        for (int j = 0; j < 2 * capacity; ++j)
+            if (hipEventCreate(&t->ev[q][j]) != hipSuccess) {
+                t->ev[q][j] = nullptr;
+                moe_timer_destroy(t);
+                return MOE_EHIP;
+            }
+    }
+    *out = t;
+    return MOE_OK;
+}
+
+int moe_timer_destroy(moe_timer_t *t)
+{
+    if (!t) return MOE_EINVAL;
+    for (int q = 0; q < MOE_STAGE_N; ++q) {
+        if (!t->ev[q]) continue;
+        for (int j = 0; j < 2 * t->capacity; ++j)
+            if (t->ev[q][j]) (void)hipEventDestroy(t->ev[q][j]);
+        delete[] t->ev[q];
+    }
+    delete t;
+    return MOE_OK;
+}
+
+int moe_timer_read(moe_timer_t *t, double *total_ms, int64_t *launches)
+{
+    if (!t || !total_ms || !launches) return MOE_EINVAL;
+    int rc = MOE_OK;
+    for (int q = 0; q < MOE_STAGE_N; ++q) {
+        double sum = 0.0;
+        for (int j = 0; j < t->used[q]; ++j) {
+            float ms = 0.f;
+            if (hipEventSynchronize(t->ev[q][2 * j + 1]) != hipSuccess ||
+                hipEventElapsedTime(&ms, t->ev[q][2 * j], t->ev[q][2 * j + 1]) != hipSuccess) {
+                rc = MOE_EHIP;
+                continue;
+            }
+            sum += ms;
+        }
+        total_ms[q] += sum;
+        launches[q] += t->used[q];
+        t->used[q] = 0;
+    }
+    return rc;
+}
+
+const char *moe_status_str(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported by this build";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

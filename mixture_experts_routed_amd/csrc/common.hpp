@@ -1,0 +1,70 @@
+// Device-side definitions shared by the gfx950 kernels of the routed MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kPlanBlock = 1024;     // entries per plan block, one per thread
+constexpr int kMaxExperts = 1024;    // LDS counters per plan block
+
+// meta[] fields (values fixed by the public header's enum moe_meta_field)
+enum : int {
+    kMetaNent = 0, kMetaNblk, kMetaNr, kMetaNt, kMetaNactive, kMetaMaxcnt, kMetaNskip,
+    kMetaNbad, kMetaTm, kMetaE, kMetaK, kMetaN
+};
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// A work item of the grouped FFN: one expert's run of at most 16*MT rows.
+struct WorkItem {
+    int32_t expert;
+    int32_t row0;
+    int32_t nrows;
+    int32_t pad;
+};
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// inclusive prefix sum across the 64 lanes of a wave
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Workgroups of a 1-D grid are dealt to the 8 XCDs round-robin in blockIdx
+// order. Give each XCD one contiguous range of the first `nlogical` logical
+// block indices (so neighbouring logical blocks share that XCD's L2), with
+// the surplus blocks of a host-sized grid at the end of each XCD's queue.
+// Returns -1 for a surplus block. gridDim.x must be a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block(int nlogical)
+{
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int per = (nlogical + 7) >> 3;
+    const int lb = xcd * per + local;
+    return (local < per && lb < nlogical) ? lb : -1;
+}
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+// Activation gather and fixed-order combine for gfx950. Both are HBM-bound
+// copies/reductions: one wavefront per row, 16-byte (dwordx4) accesses.
+//
+// Gather source: "Round 4 Track C: Prefill MoE Plan ... & Epilogue / Gather
+// Audit", section 1, finding 4 -- the routed rows are copied from the
+// half-precision activation with wide vector loads and stores, bit for bit.
+// Combine source: "Batched resident MoE experts on Apple Silicon: a flat
+// parallel expert pass", section 3 -- a fixed per-token top-k summation order
+// keeps the result bit-identical from run to run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
+
+// xs[r] = x[stok[r]] (bit copy) for r < min(meta[NR], max_rows); zeros on pad
+// rows. vpr = 16-byte vectors per row.
+__global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int T, int vpr,
+                                                const int32_t *__restrict__ stok,
+                                                const int32_t *__restrict__ meta, int64_t max_rows,
+                                                uint4 *__restrict__ xs)
+{
+    const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int64_t nr = min((int64_t)meta[kMetaNr], max_rows);
+    if (r >= nr) return;
+    const int lane = threadIdx.x & 63;
+    const int t = stok[r];
+    uint4 *dst = xs + r * vpr;
+    if ((unsigned)t < (unsigned)T) {
+        const uint4 *src = x + (int64_t)t * vpr;
+        int j = lane;
+        for (; j + 3 * kWave < vpr; j += 4 * kWave) {  // 4 loads in flight per lane
+            const uint4 a = src[j], b = src[j + kWave], c = src[j + 2 * kWave],
+                        d = src[j + 3 * kWave];
+            dst[j] = a;
+            dst[j + kWave] = b;
+            dst[j + 2 * kWave] = c;
+            dst[j + 3 * kWave] = d;
+        }
+        for (; j < vpr; j += kWave) dst[j] = src[j];
+    } else {
+        for (int j = lane; j < vpr; j += kWave) dst[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// out[t] = (((+0 + y[pos[tK]]) + y[pos[tK+1]]) + ...) in fp32, k ascending,
+// pos < 0 or >= max_rows skipped. vpr = float4 per row. Each lane owns up
+// to 4 float4 columns of a chunk of 256 float4, so the row chunk of every k
+// is one 4 KB wave-wide read.
+__global__ __launch_bounds__(256) void k_combine(const float4 *__restrict__ y, int64_t max_rows,
+                                                 int vpr, const int32_t *__restrict__ pos, int T,
+                                                 int K, float4 *__restrict__ out)
+{
+    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t *p = pos + (int64_t)t * K;
+    for (int j0 = 0; j0 < vpr; j0 += 4 * kWave) {
+        float4 acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = 0; k < K; ++k) {
+            const int r = p[k];
+            if (r < 0 || r >= max_rows) continue;
+            const float4 *src = y + (int64_t)r * vpr;
+            float4 v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + lane + q * kWave;
+                v[q] = (j < vpr) ? src[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[q].x += v[q].x;
+                acc[q].y += v[q].y;
+                acc[q].z += v[q].z;
+                acc[q].w += v[q].w;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + lane + q * kWave;
+            if (j < vpr) out[(int64_t)t * vpr + j] = acc[q];
+        }
+    }
+}
+
+hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int32_t *stok,
+                         const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s)
+{
+    const int vpr = d * elem_bytes / 16;
+    const int64_t blocks = (max_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const uint4 *>(x), T, vpr, stok, meta, max_rows,
+                       static_cast<uint4 *>(xs));
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K,
+                          int d, float *out, hipStream_t s)
+{
+    const int vpr = d / 4;
+    const int blocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(y), max_rows, vpr, pos, T, K,
+                       reinterpret_cast<float4 *>(out));
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,40 @@
+// Host launchers of the routed MoE kernels (internal C++ interface between the
+// kernel sources and the C ABI in abi.cpp). Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- plan: histogram, scan + pad fill, placement ----
+hipError_t launch_hist(const int32_t *ids, int nent, int E, int nblk, int32_t *bcnt, hipStream_t s);
+hipError_t launch_scan(const int32_t *bcnt, int nblk, int E, int K, int tm, int nent, int32_t *cnt,
+                       int32_t *eoff, int32_t *boff, int32_t *tiles, int32_t *stok, float *sw,
+                       int32_t *meta, hipStream_t s);
+hipError_t launch_place(const int32_t *ids, const float *w, int nent, int E, int K, int nblk,
+                        const int32_t *eoff, const int32_t *boff, int32_t *stok, float *sw,
+                        int32_t *pos, hipStream_t s);
+
+// ---- gather and combine ----
+hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int32_t *stok,
+                         const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s);
+hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K,
+                          int d, float *out, hipStream_t s);
+
+// ---- grouped expert FFN ----
+// rows per work item of the grouped GEMMs
+int ffn_rows_per_item();
+// bound on the number of work items for a plan of max_rows rows
+int64_t ffn_max_items(int E, int tm, int64_t max_rows);
+size_t ffn_scratch_bytes(int E, int tm, int64_t max_rows);
+hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
+                           int64_t max_items, hipStream_t s);
+hipError_t launch_gateup(int dtype, const void *xs, const void *wg, const void *wu, int d, int f,
+                         const void *scratch, int64_t max_items, void *h, hipStream_t s);
+hipError_t launch_down(int dtype, const void *h, const void *wd, int d, int f, const int32_t *stok,
+                       const float *sw, const void *scratch, int64_t max_items, float *y,
+                       hipStream_t s);
+
+}  // namespace moe

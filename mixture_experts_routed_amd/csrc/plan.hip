@@ -1,0 +1,220 @@
+// Routing plan for gfx950: per-block expert histogram, one-workgroup scan
+// with the pad-row fill, and a stable placement ranked by wavefront ballots.
+//
+// Source: "Round 4 Track C: Prefill MoE Plan (mm_clear + mm_hist + mm_scan +
+// mm_place) & Epilogue / Gather Audit", section 1, findings 1-3:
+//  - the histogram zeroes its own LDS counters and stores every per-block
+//    count, so nothing has to clear it beforehand (finding 1);
+//  - the scan, one workgroup with one lane per expert, also marks its
+//    expert's pad rows -1, which removes the separate clear kernel (finding 1);
+//  - the placement rank of an entry is the number of earlier same-expert
+//    entries in its block; a serial loop over the block was the bottleneck
+//    (finding 2); histogram and scan stay separate launches because one
+//    workgroup cannot fill the GPU (finding 3).
+// Here the rank comes from ceil(log2 E) wavefront ballots that build each
+// lane's equal-expert mask (AMD has no match instruction), a popcount below
+// the lane, and a per-(expert, wave) byte table in LDS for the waves before.
+// That is exact for any multiplicity, unlike a packed-nibble counter, which
+// relies on top-10 routing to bound the count per sub-block.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// bcnt[b][0..E-1]: entries of each expert in block b; bcnt[b][E]: ids == -1;
+// bcnt[b][E+1]: other ids outside [0, E). Row stride E+2.
+__global__ __launch_bounds__(kPlanBlock) void k_hist(const int32_t *__restrict__ ids, int nent,
+                                                     int E, int32_t *__restrict__ bcnt)
+{
+    __shared__ int h[kMaxExperts + 2];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E + 2; e += kPlanBlock) h[e] = 0;
+    __syncthreads();
+    const int i = blockIdx.x * kPlanBlock + tid;
+    if (i < nent) {
+        const int e = ids[i];
+        const int slot = (e == -1) ? E : ((unsigned)e < (unsigned)E ? e : E + 1);
+        atomicAdd(&h[slot], 1);
+    }
+    __syncthreads();
+    int32_t *row = bcnt + (size_t)blockIdx.x * (E + 2);
+    for (int e = tid; e < E + 2; e += kPlanBlock) row[e] = h[e];
+}
+
+// One workgroup, lane e owns expert e: column scan of bcnt over the blocks
+// (boff, cnt), padded rows, exclusive scan over experts (eoff), pad fill,
+// tiles and meta.
+__global__ __launch_bounds__(kPlanBlock) void k_scan(
+    const int32_t *__restrict__ bcnt, int nblk, int E, int K, int tm, int nent,
+    int32_t *__restrict__ cnt, int32_t *__restrict__ eoff, int32_t *__restrict__ boff,
+    int32_t *__restrict__ tiles, int32_t *__restrict__ stok, float *__restrict__ sw,
+    int32_t *__restrict__ meta)
+{
+    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int E2 = E + 2;
+
+    int run = 0;
+    if (tid < E) {
+        int b = 0;
+        for (; b + 8 <= nblk; b += 8) {  // 8 independent loads in flight
+            int v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = bcnt[(size_t)(b + q) * E2 + tid];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                boff[(size_t)(b + q) * E + tid] = run;
+                run += v[q];
+            }
+        }
+        for (; b < nblk; ++b) {
+            const int v = bcnt[(size_t)b * E2 + tid];
+            boff[(size_t)b * E + tid] = run;
+            run += v;
+        }
+    }
+    // skipped / bad totals: block-wide sums over the two extra columns
+    int skip = 0, bad = 0;
+    for (int b = tid; b < nblk; b += kPlanBlock) {
+        skip += bcnt[(size_t)b * E2 + E];
+        bad += bcnt[(size_t)b * E2 + E + 1];
+    }
+
+    const int c = run;
+    const int rows = (c + tm - 1) / tm * tm;
+    const int incl = wave_inclusive_scan(rows, lane);
+    const int act = wave_sum(c > 0 ? 1 : 0);
+    const int mx = wave_max(c);
+    skip = wave_sum(skip);
+    bad = wave_sum(bad);
+    if (lane == 63) s_sum[wv] = incl;
+    if (lane == 0) {
+        s_act[wv] = act;
+        s_max[wv] = mx;
+        s_skip[wv] = skip;
+        s_bad[wv] = bad;
+    }
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int v = s_sum[q];
+        before += (q < wv) ? v : 0;
+        total += v;
+    }
+    const int start = before + incl - rows;  // exclusive prefix of padded rows
+
+    if (tid < E) {
+        cnt[tid] = c;
+        eoff[tid] = start;
+        for (int r = start + c; r < start + rows; ++r) {  // 0..tm-1 pad rows
+            stok[r] = -1;
+            sw[r] = 0.0f;
+        }
+        for (int j = start / tm; j < (start + rows) / tm; ++j) tiles[j] = tid;
+    }
+    if (tid == 0) {
+        int nact = 0, maxc = 0, nskip = 0, nbad = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            nact += s_act[q];
+            maxc = max(maxc, s_max[q]);
+            nskip += s_skip[q];
+            nbad += s_bad[q];
+        }
+        eoff[E] = total;
+        meta[kMetaNent] = nent;
+        meta[kMetaNblk] = nblk;
+        meta[kMetaNr] = total;
+        meta[kMetaNt] = total / tm;
+        meta[kMetaNactive] = nact;
+        meta[kMetaMaxcnt] = maxc;
+        meta[kMetaNskip] = nskip;
+        meta[kMetaNbad] = nbad;
+        meta[kMetaTm] = tm;
+        meta[kMetaE] = E;
+        meta[kMetaK] = K;
+    }
+}
+
+// sum of the bytes 0..n-1 of a 16-byte value (n in 0..15)
+__device__ __forceinline__ int bytes_below(uint4 v, int n)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    int s = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += (q < n) ? (int)((w[q >> 2] >> (8 * (q & 3))) & 0xffu) : 0;
+    return s;
+}
+
+// One workgroup per block of 1024 entries, one entry per lane.
+// row(i) = eoff[e] + boff[b][e] + (same-expert entries in earlier waves of
+// the block) + (same-expert lanes below this one in the wave).
+__global__ __launch_bounds__(kPlanBlock) void k_place(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int nent, int E, int K, int nbits,
+    const int32_t *__restrict__ eoff, const int32_t *__restrict__ boff, int32_t *__restrict__ stok,
+    float *__restrict__ sw, int32_t *__restrict__ pos)
+{
+    __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int e = tid; e < E; e += kPlanBlock) wc[e] = make_uint4(0u, 0u, 0u, 0u);
+
+    const int i = blockIdx.x * kPlanBlock + tid;
+    const bool inb = i < nent;
+    const int e = inb ? ids[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+
+    // lanes holding the same expert: AND over the id bits of (ballot of lanes
+    // whose bit is set) or its complement
+    uint64_t same = __ballot(valid);
+    for (int p = 0; p < nbits; ++p) {
+        const bool bit = (e >> p) & 1;
+        const uint64_t bl = __ballot(bit);
+        same &= bit ? bl : ~bl;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(same & below);
+    const int count = __popcll(same);
+
+    __syncthreads();  // wc zeroed
+    if (valid && rank == 0) reinterpret_cast<unsigned char *>(wc)[e * 16 + wv] = (unsigned char)count;
+    __syncthreads();
+
+    if (valid) {
+        const int before = bytes_below(wc[e], wv);
+        const int row = eoff[e] + boff[(size_t)blockIdx.x * E + e] + before + rank;
+        pos[i] = row;
+        stok[row] = i / K;
+        sw[row] = w[i];
+    } else if (inb) {
+        pos[i] = -1;
+    }
+}
+
+hipError_t launch_hist(const int32_t *ids, int nent, int E, int nblk, int32_t *bcnt, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(kPlanBlock), 0, s, ids, nent, E, bcnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t *bcnt, int nblk, int E, int K, int tm, int nent, int32_t *cnt,
+                       int32_t *eoff, int32_t *boff, int32_t *tiles, int32_t *stok, float *sw,
+                       int32_t *meta, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kPlanBlock), 0, s, bcnt, nblk, E, K, tm, nent, cnt,
+                       eoff, boff, tiles, stok, sw, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_place(const int32_t *ids, const float *w, int nent, int E, int K, int nblk,
+                        const int32_t *eoff, const int32_t *boff, int32_t *stok, float *sw,
+                        int32_t *pos, hipStream_t s)
+{
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    hipLaunchKernelGGL(k_place, dim3(nblk), dim3(kPlanBlock), 0, s, ids, w, nent, E, K, nbits, eoff,
+                       boff, stok, sw, pos);
+    return hipGetLastError();
+}
+
+}  // namespace moe

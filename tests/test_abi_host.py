@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, computes sizes in closed form, and
+rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_routed_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_routed.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*\**\s*(moe_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_plan", "moe_gather", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = abi.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(abi.EXPORTS)
+
+
+def test_plan_sizes_closed_form():
+    z = abi.moe_plan_sizes(2048, 10, 512, 16)
+    assert (z.nent, z.nblk) == (20480, 20)
+    # ceil((20480 + 512*15) / 16) * 16
+    assert z.max_rows == (20480 + 512 * 15 + 15) // 16 * 16 == 28160
+    assert z.max_tiles == 28160 // 16
+    assert z.scratch_bytes == 20 * 514 * 4
+    z = abi.moe_plan_sizes(4, 8, 128, 16)  # fewer entries than experts
+    assert z.max_rows == (32 + 32 * 15 + 15) // 16 * 16 == 512
+
+
+def test_status_strings():
+    assert abi.moe_status_str(0) == "ok"
+    assert abi.moe_status_str(1) == "invalid argument"
+    assert abi.moe_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("T,K,E,tm,rc", [
+    (0, 1, 8, 16, 1), (4, 0, 8, 16, 1), (4, 2, 0, 16, 1), (4, 2, 8, 0, 1),
+    (4, 2, 1025, 16, 2), (2 ** 30, 4, 8, 16, 1),
+])
+def test_plan_sizes_errors(T, K, E, tm, rc):
+    z = abi.PlanSizes()
+    assert abi.lib().moe_plan_sizes(T, K, E, tm, ctypes.byref(z)) == rc
+
+
+# fake, well-aligned addresses: every call below must return before touching them
+A = 1 << 20
+
+
+def test_plan_rejects_null_misaligned_and_small_scratch():
+    L = abi.lib()
+    ok = [A] * 10
+    assert L.moe_plan(None, A, 4, 2, 8, 16, *ok[:8], A, 4096, None) == 1          # NULL ids
+    assert L.moe_plan(A + 2, A, 4, 2, 8, 16, *ok[:8], A, 4096, None) == 1         # misaligned
+    assert L.moe_plan(A, A, 4, 2, 8, 16, *ok[:8], A, 7, None) == 1                # small scratch
+    assert L.moe_plan(A, A, 4, 2, 2000, 16, *ok[:8], A, 1 << 20, None) == 2       # E too large
+
+
+def test_gather_combine_ffn_forward_reject_bad_arguments():
+    L = abi.lib()
+    assert L.moe_gather(A, 5, 4, 64, A, A, 64, A, None) == 1        # bad dtype
+    assert L.moe_gather(A, 1, 4, 60, A, A, 64, A, None) == 1        # d % 8
+    assert L.moe_gather(A + 8, 1, 4, 64, A, A, 64, A, None) == 1    # x not 16-byte aligned
+    assert L.moe_combine(A, 64, A, 4, 2, 12, A, None) == 1          # d % 8
+    assert L.moe_combine(A, 64, A, 0, 2, 16, A, None) == 1          # T < 1
+    assert L.moe_combine(A + 4, 64, A, 4, 2, 16, A, None) == 1      # y misaligned
+    need = ctypes.c_size_t()
+    assert L.moe_ffn_scratch_bytes(8, 16, 256, ctypes.byref(need)) == 0
+    args = [A, A, A, A, 1, 8, 64, 128, 16, A, A, A, A, 256, A, A, A]
+    assert L.moe_expert_ffn(*args, need.value - 1, None) == 1       # small scratch
+    bad = list(args)
+    bad[7] = 100                                                     # f % 8
+    assert L.moe_expert_ffn(*bad, need.value, None) == 1
+    bad = list(args)
+    bad[5] = 4096                                                    # E too large
+    assert L.moe_expert_ffn(*bad, 1 << 30, None) == 2
+    ws = ctypes.c_size_t()
+    assert L.moe_forward_workspace(64, 2, 8, 128, 256, 16, 0, ctypes.byref(ws)) == 0
+    fargs = [A, A, A, A, A, A, 0, 64, 2, 8, 128, 256, 16, A]
+    assert L.moe_forward(*fargs, ws.value - 1, A, None) == 1        # small workspace
+    assert L.moe_forward(A, A, A, A, A, A, 0, 64, 2, 8, 128, 256, 16, A + 128, ws.value, A,
+                         None) == 1                                   # workspace not 256-aligned
+
+
+def test_forward_layout_is_consistent():
+    L = abi.moe_forward_layout(2048, 10, 512, 2560, 768, 16, abi.MOE_F16)
+    z = abi.moe_plan_sizes(2048, 10, 512, 16)
+    offs = [L.cnt, L.eoff, L.tiles, L.stok, L.sw, L.pos, L.boff, L.meta, L.plan_scratch, L.xs, L.h,
+            L.y, L.ffn_scratch, L.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.h - L.xs >= z.max_rows * 2560 * 2
+    assert L.y - L.h >= z.max_rows * 768 * 2
+    assert L.ffn_scratch - L.y >= z.max_rows * 2560 * 4
+    assert abi.moe_forward_workspace(2048, 10, 512, 2560, 768, 16, abi.MOE_F16) == L.total
+
+
+def test_timer_rejects_bad_capacity():
+    h = ctypes.c_void_p()
+    assert abi.lib().moe_timer_create(ctypes.byref(h), 0) == 1
+    assert abi.lib().moe_timer_destroy(None) == 1
+
+
+def _gpu_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful on a machine without a GPU")
+def test_no_device_gives_ehip_without_crash():
+    # valid arguments, fake addresses, no GPU: the launch fails and the call reports it
+    L = abi.lib()
+    assert L.moe_combine(A, 64, A, 4, 2, 16, A, None) == 3
