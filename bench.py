@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock target of the CPU oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (a "
+                         "kernel of known traffic, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -127,6 +130,15 @@ def main():
     def step(tmr=None):
         abi.forward(xd, idsd, wd, wts["gate"], wts["up"], wts["down"], tm=tm, workspace=ws, out=out,
                     timer=tmr)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -33,7 +33,6 @@ namespace moe {
 
 constexpr int kMT = 4;                  // 16-row m-tiles per work item
 constexpr int kItemRows = 16 * kMT;     // rows per work item
-constexpr int kNPW = 64;                // output columns per wavefront
 constexpr int kWavesPerBlock = 4;
 constexpr size_t kCtlBytes = 256;       // scratch header (item count)
 
@@ -93,10 +92,39 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
     if (tid == 0) ctl[0] = min(total, max_items);
 }
 
-template <typename T> struct Mfma;
+// ---- raw buffer loads -----------------------------------------------------
+// A buffer resource covering exactly one operand range: loads past its end
+// return zeros without touching memory (range-checked by the hardware), which
+// zero-fills the K tail of the weights and the rows past a work item's end.
+// Word 3 = 0x00020000: raw (untyped) buffer on gfx9-family GPUs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 
-template <> struct Mfma<_Float16> {
-    static __device__ __forceinline__ float4_t run(uint4 a, uint4 b, float4_t c)
+template <int BYTES> struct Ld;
+template <> struct Ld<8> {
+    typedef uint2 type;
+    static __device__ __forceinline__ uint2 run(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+    {
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0));
+    }
+};
+template <> struct Ld<16> {
+    typedef uint4 type;
+    static __device__ __forceinline__ uint4 run(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
+    {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+    }
+};
+
+// ---- per element type: MFMA and conversion -------------------------------
+template <typename T> struct Elt;
+
+template <> struct Elt<_Float16> {
+    static constexpr int KR = 8;  // K-values per lane per MFMA
+    static __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
                                                       __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
@@ -109,8 +137,9 @@ template <> struct Mfma<_Float16> {
     }
 };
 
-template <> struct Mfma<__bf16> {
-    static __device__ __forceinline__ float4_t run(uint4 a, uint4 b, float4_t c)
+template <> struct Elt<__bf16> {
+    static constexpr int KR = 8;
+    static __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -123,11 +152,14 @@ template <> struct Mfma<__bf16> {
     }
 };
 
+template <> struct Elt<float> {
+    static constexpr int KR = 4;
+};
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// Column c (0..3) of 8 consecutive K-rows, each row holding 4 consecutive
-// 16-bit columns (.x = cols 0,1; .y = cols 2,3): 8 K-values of one column as
-// an MFMA operand (element j = K-row j).
+// 16-bit B operand: 8 consecutive K-rows of NPL columns each (row i = K-value
+// i). Column c of them, as one MFMA operand (element i = K-row i).
 __device__ __forceinline__ uint4 column_of_rows(const uint2 (&r)[8], int c)
 {
     uint32_t o[4];
@@ -140,212 +172,234 @@ __device__ __forceinline__ uint4 column_of_rows(const uint2 (&r)[8], int c)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// One wavefront per (work item, 64-column slice). Kd = reduction length
-// (d for gate/up, f for down); N = output columns (f for gate/up, d for down).
-// GATEUP: B0 = W_gate, B1 = W_up, out = H (type T). Otherwise: B0 = W_down,
-// out = Y (fp32), stok/sw used in the epilogue.
-template <typename T, bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_expert_gemm(
-    const T *__restrict__ A, const T *__restrict__ B0, const T *__restrict__ B1, int Kd, int N,
-    const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items,
-    const int32_t *__restrict__ stok, const float *__restrict__ sw, void *__restrict__ out)
+__device__ __forceinline__ uint32_t word(const uint4 &v, int q)
 {
-    const int nslices = (N + kNPW - 1) / kNPW;
-    const int nunits = ctl[0] * nslices;
-    const int lb = xcd_logical_block((nunits + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (lb < 0) return;
-    const int unit = lb * kWavesPerBlock + (threadIdx.x >> 6);
-    if (unit >= nunits) return;
+    return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
 
-    const int lane = threadIdx.x & 63;
-    const int nq = lane & 15;  // MFMA row (A) / column (B) index of this lane
-    const int kg = lane >> 4;  // which group of K-values this lane supplies
-    const WorkItem it = items[unit / nslices];
-    const int slice = unit % nslices;
-    const int nrows = it.nrows;
-    const int nmt = (nrows + 15) >> 4;
-    const int col = slice * kNPW + 4 * nq;
-    const bool colv = col < N;
-
-    const T *arow[kMT];
-    bool av[kMT];
+__device__ __forceinline__ uint4 column_of_rows(const uint4 (&r)[8], int c)
+{
+    uint32_t o[4];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        const int rl = 16 * mt + nq;
-        av[mt] = rl < nrows;
-        arow[mt] = A + (int64_t)(it.row0 + (av[mt] ? rl : 0)) * Kd;
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = word(r[2 * p], c >> 1), hi = word(r[2 * p + 1], c >> 1);
+        o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
     }
-    const int64_t wbase = (int64_t)it.expert * Kd * N + (colv ? col : 0);
-    const T *b0 = B0 + wbase;
-    const T *b1 = GATEUP ? B1 + wbase : B0;
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
 
-    float4_t acc0[kMT][4], acc1[kMT][4];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            acc0[mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
-            acc1[mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
-        }
+__device__ __forceinline__ float lanef(const uint4 &v, int q)
+{
+    return __builtin_bit_cast(float, word(v, q));
+}
 
-    if constexpr (sizeof(T) == 2) {
-        constexpr int KSTEP = 32;
-        struct Stage {
-            uint2 g[8], u[8];
-            uint4 a[kMT];
-        };
-        auto load = [&](Stage &st, int k0) {
-            const int kk = k0 + 8 * kg;
-            const bool kv = kk < Kd;
-            const int kc = kv ? kk : 0;
-            const bool bv = kv && colv;
+// Pipeline depth for NMT m-tiles: stage = 32 B-operand + 4 A-operand VGPRs,
+// accumulators = 32*NMT VGPRs; S stages + accumulators stay <= ~232.
+constexpr int stages_for(int nmt) { return nmt >= 4 ? 2 : nmt == 3 ? 3 : nmt == 2 ? 4 : 5; }
+
+// Shared A tile of one K-step: 64 rows x 32 K (16-bit) or 64 rows x 16 K
+// (fp32), 64 bytes per row, double-buffered: 2 x 4 KB of LDS per workgroup.
+constexpr int kATileBytes = kItemRows * 64;
+
+// A workgroup of 4 wavefronts computes one work item (<= 64 rows) against 4
+// adjacent column slices of 16*NPL columns, one slice per wavefront.
+//  * A (the item's rows) is shared: per K-step each wavefront loads 16 rows x
+//    64 bytes (one 16-byte load per lane) into registers, writes them to an LDS
+//    slot, and after one barrier every wavefront reads its MFMA A-fragments
+//    from LDS. One copy of A per workgroup instead of one per wavefront.
+//  * B (the weights) is private to each wavefront: lane l supplies MFMA column
+//    (l & 15) and K-group (l >> 4); it loads KR K-rows x NPL columns of each
+//    weight matrix per step (16 lanes cover one 16*NPL-column row segment) and
+//    transposes them in registers, so MFMA c produces the logical columns
+//    NPL*j + c, j = 0..15.
+//  * S-stage register ring: the loads of step s+S-1 are issued before the
+//    MFMAs of step s; the loop body is straight-line code, so they stay in
+//    flight. The per-step barrier keeps the 4 wavefronts in step, so together
+//    they read 4 adjacent row segments of every weight row.
+template <typename T, bool GATEUP, int NPL, int NMT>
+__device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__restrict__ B0,
+                                          const T *__restrict__ B1, int Kd, int N, WorkItem it,
+                                          int slice, const int32_t *__restrict__ stok,
+                                          const float *__restrict__ sw, void *__restrict__ out,
+                                          uint4 *__restrict__ a_lds)
+{
+    constexpr int ES = sizeof(T);
+    constexpr int KR = Elt<T>::KR;
+    constexpr int KSTEP = 4 * KR;
+    constexpr int NMAT = GATEUP ? 2 : 1;
+    constexpr int LB = NPL * ES;  // bytes per lane per row
+    typedef typename Ld<LB>::type RowT;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int nq = lane & 15, kg = lane >> 4;
+    const int col = slice * 16 * NPL + NPL * nq;
+    const bool slice_ok = slice * 16 * NPL < N;  // wave-uniform
+
+    // operand ranges: this expert's weight matrices (empty for a surplus
+    // slice: its loads return zeros without memory traffic), this item's rows
+    const size_t wofs = (size_t)it.expert * Kd * N;
+    const uint32_t wbytes = slice_ok ? (uint32_t)((size_t)Kd * N * ES) : 0u;
+    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + wofs, wbytes);
+    const __amdgpu_buffer_rsrc_t rb1 = make_rsrc((GATEUP ? B1 : B0) + wofs, wbytes);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
+    const uint32_t rowb = (uint32_t)N * ES;  // bytes per weight row
+    const uint32_t vcol = (uint32_t)col * ES;
+    // this thread's share of the A tile: row tid/4, 16-byte chunk tid%4
+    const int arow = tid >> 2, achunk = (tid & 3) * (16 / ES);
+    const uint32_t va0 = (uint32_t)arow * (uint32_t)Kd * ES;
+
+    float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(b0 + (int64_t)(kc + i) * N);
-                st.g[i] = bv ? v : make_uint2(0u, 0u);
-            }
-            if constexpr (GATEUP) {
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(b1 + (int64_t)(kc + i) * N);
-                    st.u[i] = bv ? v : make_uint2(0u, 0u);
-                }
-            }
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-                if (mt < nmt) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(arow[mt] + kc);
-                    st.a[mt] = (kv && av[mt]) ? v : make_uint4(0u, 0u, 0u, 0u);
-                }
-        };
-        auto compute = [&](const Stage &st) {
+            for (int c = 0; c < NPL; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Stage {
+        RowT b[NMAT][KR];
+        uint4 a;
+    };
+    auto load = [&](Stage &st, int k0) {
+        const int kk = k0 + KR * kg;
+        const uint32_t vb = vcol + (uint32_t)kk * rowb;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 fg = column_of_rows(st.g, c);
-                uint4 fu = fg;
-                if constexpr (GATEUP) fu = column_of_rows(st.u, c);
+        for (int i = 0; i < KR; ++i) st.b[0][i] = Ld<LB>::run(rb0, vb, (uint32_t)i * rowb);
+        if constexpr (GATEUP) {
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-                    if (mt < nmt) {
-                        acc0[mt][c] = Mfma<T>::run(st.a[mt], fg, acc0[mt][c]);
-                        if constexpr (GATEUP) acc1[mt][c] = Mfma<T>::run(st.a[mt], fu, acc1[mt][c]);
-                    }
-            }
-        };
-        const int nsteps = (Kd + KSTEP - 1) / KSTEP;
-        Stage s0, s1;
-        load(s0, 0);
-        int s = 0;
-        for (; s + 1 < nsteps; s += 2) {
-            load(s1, (s + 1) * KSTEP);
-            compute(s0);
-            if (s + 2 < nsteps) load(s0, (s + 2) * KSTEP);
-            compute(s1);
+            for (int i = 0; i < KR; ++i) st.b[1][i] = Ld<LB>::run(rb1, vb, (uint32_t)i * rowb);
         }
-        if (s < nsteps) compute(s0);
-    } else {
-        // fp32: v_mfma_f32_16x16x4_f32, one K-value per lane per MFMA. A lane
-        // loads 4 consecutive K of its A row and the 4 matching B rows; sub-step
-        // q uses K = k0 + 4*kg + q in both operands.
-        constexpr int KSTEP = 16;
-        struct Stage {
-            float4 g[4], u[4];
-            float4 a[kMT];
-        };
-        auto load = [&](Stage &st, int k0) {
-            const int kk = k0 + 4 * kg;
-            const bool kv = kk < Kd;
-            const int kc = kv ? kk : 0;
-            const bool bv = kv && colv;
-            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        // K past the end: the weights read as zero; zero A too so that no
+        // non-finite value of a neighbouring row can leak in as 0 * inf.
+        const int ka = k0 + achunk;
+        const uint32_t am = ka < Kd ? 0xffffffffu : 0u;
+        const uint4 v = Ld<16>::run(ra, va0 + (uint32_t)ka * ES, 0u);
+        st.a = make_uint4(v.x & am, v.y & am, v.z & am, v.w & am);
+    };
+    auto compute = [&](const Stage &st, int step) {
+        uint4 *slot = a_lds + (step & 1) * (kATileBytes / 16);
+        slot[tid] = st.a;
+        __syncthreads();
+        uint4 af[NMT];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = *reinterpret_cast<const float4 *>(b0 + (int64_t)(kc + q) * N);
-                st.g[q] = bv ? v : z;
-                if constexpr (GATEUP) {
-                    const float4 w = *reinterpret_cast<const float4 *>(b1 + (int64_t)(kc + q) * N);
-                    st.u[q] = bv ? w : z;
+        for (int mt = 0; mt < NMT; ++mt) af[mt] = slot[(16 * mt + nq) * 4 + kg];
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int c = 0; c < NPL; ++c) {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const uint4 fb = column_of_rows(st.b[m], c);
+#pragma unroll
+                    for (int mt = 0; mt < NMT; ++mt)
+                        acc[m][mt][c] = Elt<T>::mfma(af[mt], fb, acc[m][mt][c]);
                 }
             }
+        } else {
+            // fp32: sub-step q uses K = k0 + 4*kg + q in both operands
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-                if (mt < nmt) {
-                    const float4 v = *reinterpret_cast<const float4 *>(arow[mt] + kc);
-                    st.a[mt] = (kv && av[mt]) ? v : z;
-                }
-        };
-        auto compute = [&](const Stage &st) {
+            for (int q = 0; q < KR; ++q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float gq[4] = {st.g[q].x, st.g[q].y, st.g[q].z, st.g[q].w};
-                const float uq[4] = {st.u[q].x, st.u[q].y, st.u[q].z, st.u[q].w};
+                for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-                    if (mt < nmt) {
-                        const float aq = (q == 0) ? st.a[mt].x
-                                       : (q == 1) ? st.a[mt].y
-                                       : (q == 2) ? st.a[mt].z
-                                                  : st.a[mt].w;
+                    for (int c = 0; c < NPL; ++c) {
+                        const float b = lanef(st.b[m][q], c);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            acc0[mt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, gq[c], acc0[mt][c], 0, 0, 0);
-                            if constexpr (GATEUP)
-                                acc1[mt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, uq[c], acc1[mt][c], 0, 0, 0);
-                        }
+                        for (int mt = 0; mt < NMT; ++mt)
+                            acc[m][mt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                lanef(af[mt], q), b, acc[m][mt][c], 0, 0, 0);
                     }
-            }
-        };
-        const int nsteps = (Kd + KSTEP - 1) / KSTEP;
-        Stage s0, s1;
-        load(s0, 0);
-        int s = 0;
-        for (; s + 1 < nsteps; s += 2) {
-            load(s1, (s + 1) * KSTEP);
-            compute(s0);
-            if (s + 2 < nsteps) load(s0, (s + 2) * KSTEP);
-            compute(s1);
         }
-        if (s < nsteps) compute(s0);
+    };
+
+    constexpr int S = stages_for(NMT);
+    const int nsteps = (Kd + KSTEP - 1) / KSTEP;
+    Stage st[S];
+#pragma unroll
+    for (int j = 0; j < S - 1; ++j) load(st[j], j * KSTEP);
+    for (int s = 0; s < nsteps; s += S) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            // steps past the end load zero weights (no memory traffic) and add 0
+            load(st[(j + S - 1) % S], (s + j + S - 1) * KSTEP);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st[j], s + j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
-    // Epilogue. acc[mt][c][r] is the output at row 16*mt + 4*kg + r of the
+    // Epilogue: acc[m][mt][c][r] is the output at row 16*mt + 4*kg + r of the
     // item and column col + c.
-    if (!colv) return;
+    if (col >= N) return;
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        if (mt >= nmt) break;
+    for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rl = 16 * mt + 4 * kg + r;
-            if (rl >= nrows) continue;
+            if (rl >= it.nrows) continue;
             const int64_t row = it.row0 + rl;
             if constexpr (GATEUP) {
-                float hv[4];
+                float hv[NPL];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) hv[c] = silu(acc0[mt][c][r]) * acc1[mt][c][r];
+                for (int c = 0; c < NPL; ++c) hv[c] = silu(acc[0][mt][c][r]) * acc[1][mt][c][r];
                 T *H = static_cast<T *>(out) + row * N + col;
-                if constexpr (sizeof(T) == 2) {
+                if constexpr (ES == 2) {
+                    static_assert(NPL == 4, "16-bit gate/up stores 4 columns per lane");
                     *reinterpret_cast<uint2 *>(H) =
-                        make_uint2(Mfma<T>::pack2(hv[0], hv[1]), Mfma<T>::pack2(hv[2], hv[3]));
+                        make_uint2(Elt<T>::pack2(hv[0], hv[1]), Elt<T>::pack2(hv[2], hv[3]));
                 } else {
+                    static_assert(NPL == 4, "fp32 gate/up stores 4 columns per lane");
                     *reinterpret_cast<float4 *>(H) = make_float4(hv[0], hv[1], hv[2], hv[3]);
                 }
             } else {
                 if (stok[row] < 0) continue;  // pad rows are never combined
-                const float s = sw[row];
+                const float g = sw[row];
                 float *Y = static_cast<float *>(out) + row * N + col;
-                *reinterpret_cast<float4 *>(Y) =
-                    make_float4(s * acc0[mt][0][r], s * acc0[mt][1][r], s * acc0[mt][2][r],
-                                s * acc0[mt][3][r]);
+#pragma unroll
+                for (int c = 0; c < NPL; c += 4)
+                    *reinterpret_cast<float4 *>(Y + c) =
+                        make_float4(g * acc[0][mt][c][r], g * acc[0][mt][c + 1][r],
+                                    g * acc[0][mt][c + 2][r], g * acc[0][mt][c + 3][r]);
             }
         }
     }
 }
 
-static unsigned gemm_blocks(int64_t max_items, int N)
+// One workgroup per (work item, group of 4 column slices of 16*NPL).
+// Kd = reduction length (d for gate/up, f for down); N = output columns (f for
+// gate/up, d for down). GATEUP: B0 = W_gate, B1 = W_up, out = H (type T).
+// Otherwise: B0 = W_down, out = Y (fp32), stok/sw used in the epilogue.
+template <typename T, bool GATEUP, int NPL>
+__global__ __launch_bounds__(256, 2) void k_expert_gemm(
+    const T *__restrict__ A, const T *__restrict__ B0, const T *__restrict__ B1, int Kd, int N,
+    const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items,
+    const int32_t *__restrict__ stok, const float *__restrict__ sw, void *__restrict__ out)
 {
-    const int64_t units = max_items * ((N + kNPW - 1) / kNPW);
-    int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+    __shared__ uint4 a_lds[2 * kATileBytes / 16];
+    const int ngroups = (N + 64 * NPL - 1) / (64 * NPL);  // slice groups per item
+    const int lb = xcd_logical_block(ctl[0] * ngroups);
+    if (lb < 0) return;  // whole workgroup: no barrier reached
+    const WorkItem it = items[lb / ngroups];
+    // wave-uniform by construction, so the buffer descriptors live in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = (lb % ngroups) * kWavesPerBlock + wave;
+    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
+    case 1: wave_gemm<T, GATEUP, NPL, 1>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
+    case 2: wave_gemm<T, GATEUP, NPL, 2>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
+    case 3: wave_gemm<T, GATEUP, NPL, 3>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
+    default: wave_gemm<T, GATEUP, NPL, kMT>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
+    }
+}
+
+// columns per lane: gate/up 4 (64 per wave, two matrices); down 8 for 16-bit
+// types (128 per wave, one matrix), 4 for fp32
+template <typename T> constexpr int npl_down() { return sizeof(T) == 2 ? 8 : 4; }
+constexpr int kNplGateUp = 4;
+
+static unsigned gemm_blocks(int64_t max_items, int N, int npl)
+{
+    int64_t blocks = max_items * ((N + 64 * npl - 1) / (64 * npl));
     blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     return (unsigned)blocks;
 }
@@ -367,7 +421,8 @@ static hipError_t gateup_t(const void *xs, const void *wg, const void *wu, int d
     const int32_t *ctl = static_cast<const int32_t *>(scratch);
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, true>), dim3(gemm_blocks(max_items, f)), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_expert_gemm<T, true, kNplGateUp>), dim3(gemm_blocks(max_items, f, kNplGateUp)),
+                       dim3(256), 0, s,
                        static_cast<const T *>(xs), static_cast<const T *>(wg),
                        static_cast<const T *>(wu), d, f, ctl, items, nullptr, nullptr, h);
     return hipGetLastError();
@@ -381,7 +436,8 @@ static hipError_t down_t(const void *h, const void *wd, int d, int f, const int3
     const int32_t *ctl = static_cast<const int32_t *>(scratch);
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, false>), dim3(gemm_blocks(max_items, d)), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_expert_gemm<T, false, npl_down<T>()>),
+                       dim3(gemm_blocks(max_items, d, npl_down<T>())), dim3(256), 0, s,
                        static_cast<const T *>(h), static_cast<const T *>(wd), nullptr, f, d, ctl,
                        items, stok, sw, static_cast<void *>(y));
     return hipGetLastError();
