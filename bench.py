@@ -34,8 +34,114 @@ METRIC = "routed (token,expert) rows/sec per MoE layer, T=2048 E=512 top-10; pla
 HBM_PEAK_GBS = 8000.0
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_RECORD = os.path.join(PROFILES, "prefill_fp16_hbm_traffic.md")
+GEMM_SOURCES = ["mixture_experts_routed_amd/csrc/ffn.hip", "mixture_experts_routed_amd/csrc/common.hpp"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> dict:
+    """Per-kernel HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for a plain device copy of known size
+    (the --copy-calibration-mib copy in the same run). Writes a markdown summary with a
+    machine-readable record line and returns the record."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(dict)  # kernel -> dispatch -> KiB (summed over counter instances)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = vals[r["Kernel_Name"]]
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return vals
+
+    def short(name):
+        m = re.search(r"moe::(k_\w+)|_ZN3moe(\d+)(k_\w+?)I", name)
+        if "k_expert_gemm" in name:
+            kind = "gateup" if ("Lb1E" in name or "true" in name) else "down"
+            return f"k_expert_gemm/{kind}"
+        if m:
+            return m.group(1) or m.group(3)
+        return name[:40]
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = None
+    cf = [v for v in fetch.get(COPY_KERNEL, {}).values()]
+    cw = [v for v in write.get(COPY_KERNEL, {}).values()]
+    # the calibration copy is the large one; its size in KiB comes from WRITE_SIZE's own count
+    copy_f, copy_w = max(cf), max(cw)
+    mib = round(copy_w / 1024)
+    copy_kib = mib * 1024
+    kf, kw = copy_kib / copy_f, copy_kib / copy_w
+    rows, rec = [], {"source_hash": gemm_source_hash(), "fetch_scale": kf, "write_scale": kw,
+                     "copy_mib": mib, "kernels": {}}
+    for k in sorted(set(fetch) | set(write)):
+        if k == COPY_KERNEL or "elementwise" in k:
+            continue
+        f = list(fetch.get(k, {}).values())
+        w = list(write.get(k, {}).values())
+        fb = kf * sum(f) / max(len(f), 1) * 1024
+        wb = kw * sum(w) / max(len(w), 1) * 1024
+        rec["kernels"][short(k)] = {"read_bytes": fb, "write_bytes": wb, "dispatches": len(f)}
+        rows.append((short(k), len(f), fb / 1e6, wb / 1e6))
+    lines = [
+        "# HBM traffic per dispatch: prefill_fp16 layer (T=2048, d=2560, E=512, top-10, f=768, fp16)",
+        "",
+        "Commands (from the repository root on one MI355X; each counter in its own run):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"Calibration: a plain {mib} MiB device copy in the same runs read FETCH_SIZE = "
+        f"{copy_f:.0f} KiB and WRITE_SIZE = {copy_w:.0f} KiB, so reads are scaled x{kf:.3f} "
+        f"and writes x{kw:.3f}.",
+        "",
+        "| kernel | dispatches | read MB / dispatch | written MB / dispatch |",
+        "|---|---:|---:|---:|",
+    ] + [f"| `{k}` | {n} | {r:.2f} | {w:.2f} |" for k, n, r, w in rows] + [
+        "",
+        f"Kernel source hash (grouped GEMM sources at the time of the runs): {rec['source_hash']}",
+        "",
+        "traffic-record: " + json.dumps(rec),
+        "",
+    ]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines))
+    return rec
+
+
+def recorded_traffic(kernel: str):
+    """Calibrated HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when that summary was taken on different grouped-GEMM sources than the ones built now."""
+    try:
+        for line in open(TRAFFIC_RECORD):
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec["source_hash"] != gemm_source_hash():
+                    return None
+                k = rec["kernels"][kernel]
+                return k["read_bytes"] + k["write_bytes"]
+    except (OSError, KeyError, ValueError):
+        return None
+    return None
 
 
 def parse():
@@ -47,6 +153,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock target of the CPU oracle sample")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the calibrated HBM-traffic summary from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run) and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in that summary")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a "
                          "kernel of known traffic, to scale hardware byte counters)")
@@ -93,6 +203,10 @@ def cpu_baseline(cfg, ids, w, x, seconds):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        rec = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_RECORD, args.pmc_command)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the layer is measured at one GPU's share; see the design notes on sharding)",
@@ -171,7 +285,8 @@ def main():
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
         "roofline": {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": gu_bytes},
+                     "traffic": recorded_traffic("k_expert_gemm/gateup"),
+                     "algorithmic_bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, ids, w, x, args.cpu_seconds)
