@@ -103,21 +103,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              0x00020000);
 }
 
-template <int BYTES> struct Ld;
-template <> struct Ld<8> {
+// Cache policy of a buffer load: 0 = default; kNT = non-temporal (the weights
+// are read exactly once, so they should not displace the reused row tiles).
+constexpr int kNT = 2;
+
+template <int BYTES, int POLICY = 0> struct Ld;
+template <int POLICY> struct Ld<8, POLICY> {
     typedef uint2 type;
     static __device__ __forceinline__ uint2 run(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
     {
-        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0));
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, v, s, POLICY));
     }
 };
-template <> struct Ld<16> {
+template <int POLICY> struct Ld<16, POLICY> {
     typedef uint4 type;
     static __device__ __forceinline__ uint4 run(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s)
     {
-        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, POLICY));
     }
 };
+
+// stores of outputs that this kernel does not read again: non-temporal
+__device__ __forceinline__ void store_nt(float4 *p, float4 v)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
+{
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u2{v.x, v.y}, reinterpret_cast<u2 *>(p));
+}
 
 // ---- per element type: MFMA and conversion -------------------------------
 template <typename T> struct Elt;
@@ -177,17 +193,6 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int q)
     return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ uint4 column_of_rows(const uint4 (&r)[8], int c)
-{
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = word(r[2 * p], c >> 1), hi = word(r[2 * p + 1], c >> 1);
-        o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 __device__ __forceinline__ float lanef(const uint4 &v, int q)
 {
     return __builtin_bit_cast(float, word(v, q));
@@ -221,27 +226,37 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
                                           const T *__restrict__ B1, int Kd, int N, WorkItem it,
                                           int slice, const int32_t *__restrict__ stok,
                                           const float *__restrict__ sw, void *__restrict__ out,
-                                          uint4 *__restrict__ a_lds)
+                                          uint4 *__restrict__ a_lds, float2 *__restrict__ rinfo)
 {
     constexpr int ES = sizeof(T);
     constexpr int KR = Elt<T>::KR;
     constexpr int KSTEP = 4 * KR;
-    constexpr int NMAT = GATEUP ? 2 : 1;
+    constexpr int NMAT = 2;       // two B streams (see above)
     constexpr int LB = NPL * ES;  // bytes per lane per row
     typedef typename Ld<LB>::type RowT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int nq = lane & 15, kg = lane >> 4;
-    const int col = slice * 16 * NPL + NPL * nq;
-    const bool slice_ok = slice * 16 * NPL < N;  // wave-uniform
+    // GATEUP: slice = 16*NPL columns of both W_gate and W_up. Down: slice =
+    // 2*16*NPL columns of W_down, as two halves 16*NPL columns apart, so that
+    // each fp32 store instruction of the epilogue covers whole 64-byte runs.
+    constexpr int SW = GATEUP ? 16 * NPL : 32 * NPL;  // columns per slice
+    constexpr int HALF = GATEUP ? 0 : 16 * NPL;       // column offset of stream 1
+    const int col = slice * SW + NPL * nq;
+    const bool slice_ok = slice * SW < N;  // wave-uniform
 
     // operand ranges: this expert's weight matrices (empty for a surplus
     // slice: its loads return zeros without memory traffic), this item's rows
     const size_t wofs = (size_t)it.expert * Kd * N;
     const uint32_t wbytes = slice_ok ? (uint32_t)((size_t)Kd * N * ES) : 0u;
     const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + wofs, wbytes);
-    const __amdgpu_buffer_rsrc_t rb1 = make_rsrc((GATEUP ? B1 : B0) + wofs, wbytes);
+    // (Kd*N >= 64 >= HALF, so the second range never underflows; readfirstlane
+    // keeps the wave-uniform value in an SGPR)
+    const uint32_t wbytes1 = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(slice_ok ? (uint32_t)((size_t)Kd * N * ES - (size_t)HALF * ES) : 0u));
+    const __amdgpu_buffer_rsrc_t rb1 =
+        GATEUP ? make_rsrc(B1 + wofs, wbytes) : make_rsrc(B0 + wofs + HALF, wbytes1);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
     const uint32_t rowb = (uint32_t)N * ES;  // bytes per weight row
@@ -249,6 +264,16 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
     // this thread's share of the A tile: row tid/4, 16-byte chunk tid%4
     const int arow = tid >> 2, achunk = (tid & 3) * (16 / ES);
     const uint32_t va0 = (uint32_t)arow * (uint32_t)Kd * ES;
+
+    if constexpr (!GATEUP) {
+        // router weight and token of the item's rows for the epilogue (made
+        // visible to all wavefronts by the barriers of the K loop)
+        if (tid < kItemRows) {
+            const bool ok = tid < it.nrows;
+            const int64_t r = it.row0 + (ok ? tid : 0);
+            rinfo[tid] = make_float2(ok ? sw[r] : 0.f, __int_as_float(ok ? stok[r] : -1));
+        }
+    }
 
     float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
@@ -266,11 +291,9 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
         const int kk = k0 + KR * kg;
         const uint32_t vb = vcol + (uint32_t)kk * rowb;
 #pragma unroll
-        for (int i = 0; i < KR; ++i) st.b[0][i] = Ld<LB>::run(rb0, vb, (uint32_t)i * rowb);
-        if constexpr (GATEUP) {
+        for (int i = 0; i < KR; ++i) st.b[0][i] = Ld<LB, kNT>::run(rb0, vb, (uint32_t)i * rowb);
 #pragma unroll
-            for (int i = 0; i < KR; ++i) st.b[1][i] = Ld<LB>::run(rb1, vb, (uint32_t)i * rowb);
-        }
+        for (int i = 0; i < KR; ++i) st.b[1][i] = Ld<LB, kNT>::run(rb1, vb, (uint32_t)i * rowb);
         // K past the end: the weights read as zero; zero A too so that no
         // non-finite value of a neighbouring row can leak in as 0 * inf.
         const int ka = k0 + achunk;
@@ -346,21 +369,24 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
                 T *H = static_cast<T *>(out) + row * N + col;
                 if constexpr (ES == 2) {
                     static_assert(NPL == 4, "16-bit gate/up stores 4 columns per lane");
-                    *reinterpret_cast<uint2 *>(H) =
-                        make_uint2(Elt<T>::pack2(hv[0], hv[1]), Elt<T>::pack2(hv[2], hv[3]));
+                    store_nt(reinterpret_cast<uint2 *>(H),
+                             make_uint2(Elt<T>::pack2(hv[0], hv[1]), Elt<T>::pack2(hv[2], hv[3])));
                 } else {
                     static_assert(NPL == 4, "fp32 gate/up stores 4 columns per lane");
-                    *reinterpret_cast<float4 *>(H) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                    store_nt(reinterpret_cast<float4 *>(H), make_float4(hv[0], hv[1], hv[2], hv[3]));
                 }
             } else {
-                if (stok[row] < 0) continue;  // pad rows are never combined
-                const float g = sw[row];
+                static_assert(NPL == 4, "down stores 4 + 4 columns per lane");
+                const float2 ri = rinfo[rl];
+                if (__float_as_int(ri.y) < 0) continue;  // pad rows are never combined
+                const float g = ri.x;
                 float *Y = static_cast<float *>(out) + row * N + col;
 #pragma unroll
-                for (int c = 0; c < NPL; c += 4)
-                    *reinterpret_cast<float4 *>(Y + c) =
-                        make_float4(g * acc[0][mt][c][r], g * acc[0][mt][c + 1][r],
-                                    g * acc[0][mt][c + 2][r], g * acc[0][mt][c + 3][r]);
+                for (int m = 0; m < NMAT; ++m)
+                    if (col + m * HALF < N)
+                        store_nt(reinterpret_cast<float4 *>(Y + m * HALF),
+                                 make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
+                                             g * acc[m][mt][2][r], g * acc[m][mt][3][r]));
             }
         }
     }
@@ -377,7 +403,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(
     const int32_t *__restrict__ stok, const float *__restrict__ sw, void *__restrict__ out)
 {
     __shared__ uint4 a_lds[2 * kATileBytes / 16];
-    const int ngroups = (N + 64 * NPL - 1) / (64 * NPL);  // slice groups per item
+    __shared__ float2 rinfo[kItemRows];
+    constexpr int SW = GATEUP ? 16 * NPL : 32 * NPL;      // columns per slice
+    const int ngroups = (N + 4 * SW - 1) / (4 * SW);      // slice groups per item
     const int lb = xcd_logical_block(ctl[0] * ngroups);
     if (lb < 0) return;  // whole workgroup: no barrier reached
     const WorkItem it = items[lb / ngroups];
@@ -385,21 +413,21 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = (lb % ngroups) * kWavesPerBlock + wave;
     switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wave_gemm<T, GATEUP, NPL, 1>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
-    case 2: wave_gemm<T, GATEUP, NPL, 2>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
-    case 3: wave_gemm<T, GATEUP, NPL, 3>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
-    default: wave_gemm<T, GATEUP, NPL, kMT>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds); break;
+    case 1: wave_gemm<T, GATEUP, NPL, 1>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 2: wave_gemm<T, GATEUP, NPL, 2>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 3: wave_gemm<T, GATEUP, NPL, 3>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    default: wave_gemm<T, GATEUP, NPL, kMT>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
     }
 }
 
-// columns per lane: gate/up 4 (64 per wave, two matrices); down 8 for 16-bit
-// types (128 per wave, one matrix), 4 for fp32
-template <typename T> constexpr int npl_down() { return sizeof(T) == 2 ? 8 : 4; }
+// columns per lane and B stream: 4 (gate/up: 64 columns of both matrices per
+// wave; down: 2 x 64 columns of W_down per wave)
+template <typename T> constexpr int npl_down() { return 4; }
 constexpr int kNplGateUp = 4;
 
-static unsigned gemm_blocks(int64_t max_items, int N, int npl)
+static unsigned gemm_blocks(int64_t max_items, int N, int slice_cols)
 {
-    int64_t blocks = max_items * ((N + 64 * npl - 1) / (64 * npl));
+    int64_t blocks = max_items * ((N + 4 * slice_cols - 1) / (4 * slice_cols));
     blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
     return (unsigned)blocks;
 }
@@ -421,7 +449,7 @@ static hipError_t gateup_t(const void *xs, const void *wg, const void *wu, int d
     const int32_t *ctl = static_cast<const int32_t *>(scratch);
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, true, kNplGateUp>), dim3(gemm_blocks(max_items, f, kNplGateUp)),
+    hipLaunchKernelGGL((k_expert_gemm<T, true, kNplGateUp>), dim3(gemm_blocks(max_items, f, 16 * kNplGateUp)),
                        dim3(256), 0, s,
                        static_cast<const T *>(xs), static_cast<const T *>(wg),
                        static_cast<const T *>(wu), d, f, ctl, items, nullptr, nullptr, h);
@@ -437,7 +465,7 @@ static hipError_t down_t(const void *h, const void *wd, int d, int f, const int3
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
     hipLaunchKernelGGL((k_expert_gemm<T, false, npl_down<T>()>),
-                       dim3(gemm_blocks(max_items, d, npl_down<T>())), dim3(256), 0, s,
+                       dim3(gemm_blocks(max_items, d, 32 * npl_down<T>())), dim3(256), 0, s,
                        static_cast<const T *>(h), static_cast<const T *>(wd), nullptr, f, d, ctl,
                        items, stok, sw, static_cast<void *>(y));
     return hipGetLastError();

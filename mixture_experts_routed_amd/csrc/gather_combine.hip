@@ -14,6 +14,25 @@ namespace moe {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
 
+// non-temporal accesses for data touched once here (the destination rows of
+// the gather, the expert outputs read by the combine, the layer output)
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
+{
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u4{v.x, v.y, v.z, v.w}, reinterpret_cast<u4 *>(p));
+}
+__device__ __forceinline__ void store_nt(float4 *p, float4 v)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w}, reinterpret_cast<f4 *>(p));
+}
+__device__ __forceinline__ float4 load_nt(const float4 *p)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // xs[r] = x[stok[r]] (bit copy) for r < min(meta[NR], max_rows); zeros on pad
 // rows. vpr = 16-byte vectors per row.
 __global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int T, int vpr,
@@ -33,14 +52,14 @@ __global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int
         for (; j + 3 * kWave < vpr; j += 4 * kWave) {  // 4 loads in flight per lane
             const uint4 a = src[j], b = src[j + kWave], c = src[j + 2 * kWave],
                         d = src[j + 3 * kWave];
-            dst[j] = a;
-            dst[j + kWave] = b;
-            dst[j + 2 * kWave] = c;
-            dst[j + 3 * kWave] = d;
+            store_nt(dst + j, a);
+            store_nt(dst + j + kWave, b);
+            store_nt(dst + j + 2 * kWave, c);
+            store_nt(dst + j + 3 * kWave, d);
         }
-        for (; j < vpr; j += kWave) dst[j] = src[j];
+        for (; j < vpr; j += kWave) store_nt(dst + j, src[j]);
     } else {
-        for (int j = lane; j < vpr; j += kWave) dst[j] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = lane; j < vpr; j += kWave) store_nt(dst + j, make_uint4(0u, 0u, 0u, 0u));
     }
 }
 
@@ -68,7 +87,7 @@ __global__ __launch_bounds__(256) void k_combine(const float4 *__restrict__ y, i
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int j = j0 + lane + q * kWave;
-                v[q] = (j < vpr) ? src[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[q] = (j < vpr) ? load_nt(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -81,7 +100,7 @@ __global__ __launch_bounds__(256) void k_combine(const float4 *__restrict__ y, i
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int j = j0 + lane + q * kWave;
-            if (j < vpr) out[(int64_t)t * vpr + j] = acc[q];
+            if (j < vpr) store_nt(out + (int64_t)t * vpr + j, acc[q]);
         }
     }
 }
