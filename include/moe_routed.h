@@ -193,8 +193,12 @@ int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int
 int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, size_t *bytes);
 
 /*
- * moe_forward -- one routed MoE layer: moe_plan, moe_gather, moe_expert_ffn
- * and moe_combine in sequence on one stream, intermediates in `workspace`.
+ * moe_forward -- one routed MoE layer: the results of moe_plan, moe_gather,
+ * moe_expert_ffn and moe_combine in sequence on one stream, intermediates in
+ * `workspace`. Fewer launches than calling them one by one: for T*K <= 32768
+ * the plan is one kernel that also writes the FFN's work list, and when x is
+ * smaller than 2 GiB the gate/up kernel reads its rows from x through stok
+ * (the gather is fused; the workspace's xs rows are then left unwritten).
  * In:  x [T][d] (dtype), ids [T*K], w [T*K], expert weights as above.
  * Out: out [T][d] fp32.
  * Errors: the union of the four calls' errors.
@@ -228,8 +232,10 @@ enum moe_stage {
 typedef struct moe_timer moe_timer_t;
 
 /* Create a timer that can hold `capacity` recorded calls (host object; its
- * HIP events are created on the current device). */
-int moe_timer_create(moe_timer_t **out, int capacity);
+ * HIP events are created on the current device). Only the stages whose bit
+ * (1 << stage) is set in stage_mask are timed, so that a caller timing one
+ * kernel adds no event records around the others. */
+int moe_timer_create(moe_timer_t **out, int capacity, unsigned stage_mask);
 int moe_timer_destroy(moe_timer_t *timer);
 /* Wait for the recorded events, add each stage's elapsed milliseconds into
  * total_ms[MOE_STAGE_N] and its launch count into launches[MOE_STAGE_N], then

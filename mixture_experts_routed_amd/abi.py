@@ -60,7 +60,7 @@ _SIGS = {
     "moe_forward_layout": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ForwardLayout)],
     "moe_forward": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P],
     "moe_forward_timed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P, P],
-    "moe_timer_create": [ctypes.POINTER(P), I32],
+    "moe_timer_create": [ctypes.POINTER(P), I32, ctypes.c_uint],
     "moe_timer_destroy": [P],
     "moe_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
 }
@@ -185,9 +185,12 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, works
 class Timer:
     """Per-kernel HIP-event timer of moe_forward_timed."""
 
-    def __init__(self, capacity: int = 256):
+    def __init__(self, capacity: int = 256, stages=STAGES):
         h = ctypes.c_void_p()
-        _check("moe_timer_create", lib().moe_timer_create(ctypes.byref(h), capacity))
+        mask = 0
+        for s in stages:
+            mask |= 1 << STAGES.index(s)
+        _check("moe_timer_create", lib().moe_timer_create(ctypes.byref(h), capacity, mask))
         self.handle = h
         self.total_ms = (ctypes.c_double * len(STAGES))()
         self.launches = (ctypes.c_int64 * len(STAGES))()

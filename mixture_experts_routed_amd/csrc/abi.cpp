@@ -64,6 +64,7 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
 
 struct moe_timer {
     int capacity;
+    unsigned mask;
     int used[MOE_STAGE_N];
     hipEvent_t *ev[MOE_STAGE_N];  // 2 * capacity events per stage
 };
@@ -77,7 +78,7 @@ struct Rec {
     bool on;
     Rec(moe_timer_t *t_, hipStream_t s_, int stage_) : t(t_), s(s_), stage(stage_), on(false)
     {
-        if (t && t->used[stage] < t->capacity) {
+        if (t && ((t->mask >> stage) & 1u) && t->used[stage] < t->capacity) {
             (void)hipEventRecord(t->ev[stage][2 * t->used[stage]], s);
             on = true;
         }
@@ -95,13 +96,16 @@ bool timer_room(const moe_timer_t *t)
 {
     if (!t) return true;
     for (int q = 0; q < MOE_STAGE_N; ++q)
-        if (t->used[q] >= t->capacity) return false;
+        if (((t->mask >> q) & 1u) && t->used[q] >= t->capacity) return false;
     return true;
 }
 
+// ffn_scratch != nullptr (moe_forward only): the plan also writes the grouped
+// FFN's work list when it runs as one fused launch; *items_done says so.
 int plan_impl(const int32_t *ids, const float *w, int T, int K, int E, int tm, int32_t *cnt,
               int32_t *eoff, int32_t *tiles, int32_t *stok, float *sw, int32_t *pos, int32_t *boff,
-              int32_t *meta, void *scratch, size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr)
+              int32_t *meta, void *scratch, size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr,
+              void *ffn_scratch = nullptr, bool *items_done = nullptr)
 {
     moe_plan_sizes_t z;
     const int rc = plan_sizes(T, K, E, tm, &z);
@@ -112,6 +116,17 @@ int plan_impl(const int32_t *ids, const float *w, int T, int K, int E, int tm, i
         scratch_bytes < z.scratch_bytes)
         return MOE_EINVAL;
     const int nent = (int)z.nent, nblk = (int)z.nblk;
+    if (items_done) *items_done = false;
+    if (nblk <= moe::plan_fused_max_blocks()) {
+        // one launch: histogram, scan, pad fill and placement (timed as the placement)
+        Rec r(tmr, s, MOE_STAGE_PLACE);
+        const int64_t max_items = moe::ffn_max_items(E, tm, z.max_rows);
+        if (moe::launch_plan_fused(ids, w, nent, E, K, tm, nblk, cnt, eoff, boff, tiles, stok, sw,
+                                   pos, meta, ffn_scratch, max_items, z.max_rows, s) != hipSuccess)
+            return MOE_EHIP;
+        if (items_done) *items_done = ffn_scratch != nullptr;
+        return MOE_OK;
+    }
     int32_t *bcnt = static_cast<int32_t *>(scratch);
     {
         Rec r(tmr, s, MOE_STAGE_HIST);
@@ -144,24 +159,30 @@ int gather_impl(const void *x, int dtype, int T, int d, const int32_t *stok, con
     return MOE_OK;
 }
 
+// x != nullptr (moe_forward only): the gate/up kernel reads its rows from
+// x[stok[r]] (T rows) and xs is not used.
 int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int dtype, int E,
              int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
              const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
-             size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr)
+             size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr, bool have_items = false,
+             const void *x = nullptr, int T = 0)
 {
     const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                              y, scratch, scratch_bytes);
     if (rc != MOE_OK) return rc;
     const int64_t max_items = moe::ffn_max_items(E, tm, max_rows);
-    {
+    if (!have_items) {
         Rec r(tmr, s, MOE_STAGE_WORKLIST);
         if (moe::launch_worklist(eoff, E, max_rows, scratch, max_items, s) != hipSuccess)
             return MOE_EHIP;
     }
     {
         Rec r(tmr, s, MOE_STAGE_GATEUP);
-        if (moe::launch_gateup(dtype, xs, wg, wu, d, f, scratch, max_items, h, s) != hipSuccess)
-            return MOE_EHIP;
+        const hipError_t e =
+            x ? moe::launch_gateup_gathered(dtype, x, T, stok, wg, wu, d, f, scratch, max_items, h,
+                                            s)
+              : moe::launch_gateup(dtype, xs, wg, wu, d, f, scratch, max_items, h, s);
+        if (e != hipSuccess) return MOE_EHIP;
     }
     {
         Rec r(tmr, s, MOE_STAGE_DOWN);
@@ -227,15 +248,22 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     char *b = static_cast<char *>(ws);
     auto i32 = [&](size_t off) { return reinterpret_cast<int32_t *>(b + off); };
     auto f32 = [&](size_t off) { return reinterpret_cast<float *>(b + off); };
+    bool items = false;
     rc = plan_impl(ids, w, T, K, E, tm, i32(L.cnt), i32(L.eoff), i32(L.tiles), i32(L.stok),
                    f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
-                   z.scratch_bytes, s, tmr);
+                   z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items);
     if (rc != MOE_OK) return rc;
-    rc = gather_impl(x, dtype, T, d, i32(L.stok), i32(L.meta), z.max_rows, b + L.xs, s, tmr);
-    if (rc != MOE_OK) return rc;
+    // The gate/up kernel gathers its rows from x itself when x is addressable
+    // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
+    const bool fused_gather = (size_t)T * d * elem_bytes(dtype) < ((size_t)1 << 31);
+    if (!fused_gather) {
+        rc = gather_impl(x, dtype, T, d, i32(L.stok), i32(L.meta), z.max_rows, b + L.xs, s, tmr);
+        if (rc != MOE_OK) return rc;
+    }
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
-                  moe::ffn_scratch_bytes(E, tm, z.max_rows), s, tmr);
+                  moe::ffn_scratch_bytes(E, tm, z.max_rows), s, tmr, items,
+                  fused_gather ? x : nullptr, T);
     if (rc != MOE_OK) return rc;
     return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);
 }
@@ -321,12 +349,14 @@ int moe_forward_timed(const void *x, const int32_t *ids, const float *w, const v
                         ws_bytes, out, as_stream(stream), timer);
 }
 
-int moe_timer_create(moe_timer_t **out, int capacity)
+int moe_timer_create(moe_timer_t **out, int capacity, unsigned stage_mask)
 {
     if (!out || capacity < 1 || capacity > (1 << 20)) return MOE_EINVAL;
+    if (stage_mask == 0 || (stage_mask >> MOE_STAGE_N) != 0) return MOE_EINVAL;
     moe_timer_t *t = new (std::nothrow) moe_timer_t();
     if (!t) return MOE_EINVAL;
     t->capacity = capacity;
+    t->mask = stage_mask;
     for (int q = 0; q < MOE_STAGE_N; ++q) {
         t->used[q] = 0;
         t->ev[q] = nullptr;

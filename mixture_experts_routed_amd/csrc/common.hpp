@@ -20,7 +20,12 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// A work item of the grouped FFN: one expert's run of at most 16*MT rows.
+// The grouped FFN works on items of at most kItemRows rows of one expert; its
+// scratch holds an item count (first kCtlBytes) followed by the items.
+constexpr int kItemRows = 64;
+constexpr size_t kCtlBytes = 256;
+
+// A work item of the grouped FFN: one expert's run of at most kItemRows rows.
 struct WorkItem {
     int32_t expert;
     int32_t row0;

@@ -31,10 +31,8 @@
 
 namespace moe {
 
-constexpr int kMT = 4;                  // 16-row m-tiles per work item
-constexpr int kItemRows = 16 * kMT;     // rows per work item
+constexpr int kMT = kItemRows / 16;     // 16-row m-tiles per work item
 constexpr int kWavesPerBlock = 4;
-constexpr size_t kCtlBytes = 256;       // scratch header (item count)
 
 int ffn_rows_per_item() { return kItemRows; }
 
@@ -221,8 +219,11 @@ constexpr int kATileBytes = kItemRows * 64;
 //    MFMAs of step s; the loop body is straight-line code, so they stay in
 //    flight. The per-step barrier keeps the 4 wavefronts in step, so together
 //    they read 4 adjacent row segments of every weight row.
-template <typename T, bool GATEUP, int NPL, int NMT>
-__device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__restrict__ B0,
+// GATHERED (gate/up only): A is the token activation x [a_rows][Kd] and row r
+// of the item reads x[stok[r]] -- the gather fused into the A-tile loads.
+template <typename T, bool GATEUP, bool GATHERED, int NPL, int NMT>
+__device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
+                                          const T *__restrict__ B0,
                                           const T *__restrict__ B1, int Kd, int N, WorkItem it,
                                           int slice, const int32_t *__restrict__ stok,
                                           const float *__restrict__ sw, void *__restrict__ out,
@@ -257,13 +258,22 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
         (int)(slice_ok ? (uint32_t)((size_t)Kd * N * ES - (size_t)HALF * ES) : 0u));
     const __amdgpu_buffer_rsrc_t rb1 =
         GATEUP ? make_rsrc(B1 + wofs, wbytes) : make_rsrc(B0 + wofs + HALF, wbytes1);
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
     const uint32_t rowb = (uint32_t)N * ES;  // bytes per weight row
     const uint32_t vcol = (uint32_t)col * ES;
     // this thread's share of the A tile: row tid/4, 16-byte chunk tid%4
     const int arow = tid >> 2, achunk = (tid & 3) * (16 / ES);
-    const uint32_t va0 = (uint32_t)arow * (uint32_t)Kd * ES;
+    __amdgpu_buffer_rsrc_t ra;
+    uint32_t va0;
+    if constexpr (GATHERED) {
+        // all of x (< 2 GiB, checked by the host); a pad row (token -1) or a
+        // row past the item starts at 2^31, outside the range: it reads zeros
+        ra = make_rsrc(A, (uint32_t)((size_t)a_rows * Kd * ES));
+        const int t = arow < it.nrows ? stok[it.row0 + arow] : -1;
+        va0 = (unsigned)t < (unsigned)a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
+    } else {
+        ra = make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
+        va0 = (uint32_t)arow * (uint32_t)Kd * ES;
+    }
 
     if constexpr (!GATEUP) {
         // router weight and token of the item's rows for the epilogue (made
@@ -396,9 +406,10 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, const T *__re
 // Kd = reduction length (d for gate/up, f for down); N = output columns (f for
 // gate/up, d for down). GATEUP: B0 = W_gate, B1 = W_up, out = H (type T).
 // Otherwise: B0 = W_down, out = Y (fp32), stok/sw used in the epilogue.
-template <typename T, bool GATEUP, int NPL>
+template <typename T, bool GATEUP, bool GATHERED, int NPL>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(
-    const T *__restrict__ A, const T *__restrict__ B0, const T *__restrict__ B1, int Kd, int N,
+    const T *__restrict__ A, int a_rows, const T *__restrict__ B0, const T *__restrict__ B1,
+    int Kd, int N,
     const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items,
     const int32_t *__restrict__ stok, const float *__restrict__ sw, void *__restrict__ out)
 {
@@ -413,10 +424,10 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = (lb % ngroups) * kWavesPerBlock + wave;
     switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wave_gemm<T, GATEUP, NPL, 1>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    case 2: wave_gemm<T, GATEUP, NPL, 2>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    case 3: wave_gemm<T, GATEUP, NPL, 3>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    default: wave_gemm<T, GATEUP, NPL, kMT>(A, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 1: wave_gemm<T, GATEUP, GATHERED, NPL, 1>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 2: wave_gemm<T, GATEUP, GATHERED, NPL, 2>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 3: wave_gemm<T, GATEUP, GATHERED, NPL, 3>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    default: wave_gemm<T, GATEUP, GATHERED, NPL, kMT>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
     }
 }
 
@@ -443,16 +454,22 @@ hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *s
 }
 
 template <typename T>
-static hipError_t gateup_t(const void *xs, const void *wg, const void *wu, int d, int f,
-                           const void *scratch, int64_t max_items, void *h, hipStream_t s)
+static hipError_t gateup_t(const void *a, int a_rows, const int32_t *stok, const void *wg,
+                           const void *wu, int d, int f, const void *scratch, int64_t max_items,
+                           void *h, hipStream_t s)
 {
     const int32_t *ctl = static_cast<const int32_t *>(scratch);
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, true, kNplGateUp>), dim3(gemm_blocks(max_items, f, 16 * kNplGateUp)),
-                       dim3(256), 0, s,
-                       static_cast<const T *>(xs), static_cast<const T *>(wg),
-                       static_cast<const T *>(wu), d, f, ctl, items, nullptr, nullptr, h);
+    const dim3 grid(gemm_blocks(max_items, f, 16 * kNplGateUp));
+    if (stok)  // rows gathered from x through stok
+        hipLaunchKernelGGL((k_expert_gemm<T, true, true, kNplGateUp>), grid, dim3(256), 0, s,
+                           static_cast<const T *>(a), a_rows, static_cast<const T *>(wg),
+                           static_cast<const T *>(wu), d, f, ctl, items, stok, nullptr, h);
+    else
+        hipLaunchKernelGGL((k_expert_gemm<T, true, false, kNplGateUp>), grid, dim3(256), 0, s,
+                           static_cast<const T *>(a), 0, static_cast<const T *>(wg),
+                           static_cast<const T *>(wu), d, f, ctl, items, nullptr, nullptr, h);
     return hipGetLastError();
 }
 
@@ -464,9 +481,9 @@ static hipError_t down_t(const void *h, const void *wd, int d, int f, const int3
     const int32_t *ctl = static_cast<const int32_t *>(scratch);
     const WorkItem *items =
         reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, false, npl_down<T>()>),
+    hipLaunchKernelGGL((k_expert_gemm<T, false, false, npl_down<T>()>),
                        dim3(gemm_blocks(max_items, d, 32 * npl_down<T>())), dim3(256), 0, s,
-                       static_cast<const T *>(h), static_cast<const T *>(wd), nullptr, f, d, ctl,
+                       static_cast<const T *>(h), 0, static_cast<const T *>(wd), nullptr, f, d, ctl,
                        items, stok, sw, static_cast<void *>(y));
     return hipGetLastError();
 }
@@ -474,9 +491,18 @@ static hipError_t down_t(const void *h, const void *wd, int d, int f, const int3
 hipError_t launch_gateup(int dtype, const void *xs, const void *wg, const void *wu, int d, int f,
                          const void *scratch, int64_t max_items, void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(xs, wg, wu, d, f, scratch, max_items, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(xs, wg, wu, d, f, scratch, max_items, h, s);
-    return gateup_t<float>(xs, wg, wu, d, f, scratch, max_items, h, s);
+    if (dtype == 1) return gateup_t<_Float16>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
+    if (dtype == 2) return gateup_t<__bf16>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
+    return gateup_t<float>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
+}
+
+hipError_t launch_gateup_gathered(int dtype, const void *x, int T, const int32_t *stok,
+                                  const void *wg, const void *wu, int d, int f, const void *scratch,
+                                  int64_t max_items, void *h, hipStream_t s)
+{
+    if (dtype == 1) return gateup_t<_Float16>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
+    if (dtype == 2) return gateup_t<__bf16>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
+    return gateup_t<float>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
 }
 
 hipError_t launch_down(int dtype, const void *h, const void *wd, int d, int f, const int32_t *stok,

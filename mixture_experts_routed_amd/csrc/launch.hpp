@@ -16,6 +16,14 @@ hipError_t launch_scan(const int32_t *bcnt, int nblk, int E, int K, int tm, int 
 hipError_t launch_place(const int32_t *ids, const float *w, int nent, int E, int K, int nblk,
                         const int32_t *eoff, const int32_t *boff, int32_t *stok, float *sw,
                         int32_t *pos, hipStream_t s);
+// Whole plan in one launch (each workgroup counts all entries); valid when
+// nblk <= plan_fused_max_blocks(). With ffn_scratch != nullptr it also writes
+// the grouped FFN's work list (max_items items) for rows capped at max_rows.
+int plan_fused_max_blocks();
+hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E, int K, int tm,
+                             int nblk, int32_t *cnt, int32_t *eoff, int32_t *boff, int32_t *tiles,
+                             int32_t *stok, float *sw, int32_t *pos, int32_t *meta,
+                             void *ffn_scratch, int64_t max_items, int64_t max_rows, hipStream_t s);
 
 // ---- gather and combine ----
 hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int32_t *stok,
@@ -33,6 +41,11 @@ hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *s
                            int64_t max_items, hipStream_t s);
 hipError_t launch_gateup(int dtype, const void *xs, const void *wg, const void *wu, int d, int f,
                          const void *scratch, int64_t max_items, void *h, hipStream_t s);
+// gate/up reading row r straight from x[stok[r]] (the gather fused into the
+// A-tile loads); x must be smaller than 2 GiB.
+hipError_t launch_gateup_gathered(int dtype, const void *x, int T, const int32_t *stok,
+                                  const void *wg, const void *wu, int d, int f, const void *scratch,
+                                  int64_t max_items, void *h, hipStream_t s);
 hipError_t launch_down(int dtype, const void *h, const void *wd, int d, int f, const int32_t *stok,
                        const float *sw, const void *scratch, int64_t max_items, float *y,
                        hipStream_t s);

@@ -191,6 +191,194 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused plan for up to kFusedMaxBlocks blocks: one launch instead of three.
+// Each workgroup (block b of 1024 entries) counts every entry of the layer
+// into LDS -- per-expert totals and the counts of the blocks before b -- so it
+// knows the padded expert offsets and its own block offsets without waiting
+// for the other workgroups; then it places its own entries exactly as k_place
+// does. Workgroup 0 also writes the layer-wide outputs (cnt, eoff, tiles, pad
+// rows, meta) and, when asked, the grouped FFN's work list. The redundant
+// counting costs nblk * nent LDS atomics in total (20 x 20,480 at T=2048,
+// top-10), far less than two extra dependent launches.
+constexpr int kFusedMaxBlocks = 32;
+
+__global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int nent, int E, int K, int tm,
+    int nbits, int32_t *__restrict__ cnt, int32_t *__restrict__ eoff, int32_t *__restrict__ boff,
+    int32_t *__restrict__ tiles, int32_t *__restrict__ stok, float *__restrict__ sw,
+    int32_t *__restrict__ pos, int32_t *__restrict__ meta, int32_t *__restrict__ ctl,
+    WorkItem *__restrict__ items, int max_items, int max_rows)
+{
+    __shared__ int s_tot[kMaxExperts], s_before[kMaxExperts], s_eoff[kMaxExperts];
+    __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
+    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_isum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x;
+    for (int e = tid; e < E; e += kPlanBlock) {
+        s_tot[e] = 0;
+        s_before[e] = 0;
+        wc[e] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+
+    // 1. histogram of all entries, and of the entries before this block
+    const int bstart = b * kPlanBlock;
+    int skip = 0, bad = 0;
+    constexpr int U = 16;  // loads in flight per lane before their atomics
+    for (int i0 = tid; i0 < nent; i0 += U * kPlanBlock) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kPlanBlock;
+            v[u] = i < nent ? ids[i] : -2;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kPlanBlock;
+            const int e = v[u];
+            if ((unsigned)e < (unsigned)E) {
+                atomicAdd(&s_tot[e], 1);
+                if (i < bstart) atomicAdd(&s_before[e], 1);
+            } else if (i < nent) {
+                skip += (e == -1);
+                bad += (e != -1);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. padded rows and their exclusive scan over experts (lane e = expert e)
+    const int c = tid < E ? s_tot[tid] : 0;
+    const int rows = (c + tm - 1) / tm * tm;
+    const int incl = wave_inclusive_scan(rows, lane);
+    const int act = wave_sum(c > 0 ? 1 : 0);
+    const int mx = wave_max(c);
+    skip = wave_sum(skip);
+    bad = wave_sum(bad);
+    // work items of this expert (only needed by workgroup 0)
+    const int nit = (rows + kItemRows - 1) / kItemRows;
+    const int iincl = wave_inclusive_scan(nit, lane);
+    if (lane == 63) {
+        s_sum[wv] = incl;
+        s_isum[wv] = iincl;
+    }
+    if (lane == 0) {
+        s_act[wv] = act;
+        s_max[wv] = mx;
+        s_skip[wv] = skip;
+        s_bad[wv] = bad;
+    }
+    __syncthreads();
+    int before = 0, total = 0, ibefore = 0, itotal = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int v = s_sum[q], iv = s_isum[q];
+        before += (q < wv) ? v : 0;
+        total += v;
+        ibefore += (q < wv) ? iv : 0;
+        itotal += iv;
+    }
+    const int start = before + incl - rows;
+    if (tid < E) {
+        s_eoff[tid] = start;
+        boff[(size_t)b * E + tid] = s_before[tid];
+    }
+    if (b == 0) {
+        if (tid < E) {
+            cnt[tid] = c;
+            eoff[tid] = start;
+            for (int r = start + c; r < start + rows; ++r) {  // 0..tm-1 pad rows
+                stok[r] = -1;
+                sw[r] = 0.0f;
+            }
+            for (int j = start / tm; j < (start + rows) / tm; ++j) tiles[j] = tid;
+            if (items) {
+                const int istart = ibefore + iincl - nit;
+                for (int q = 0; q < nit; ++q) {
+                    const int idx = istart + q;
+                    const int r0 = start + q * kItemRows;
+                    if (idx < max_items && r0 < max_rows) {
+                        WorkItem it;
+                        it.expert = tid;
+                        it.row0 = r0;
+                        it.nrows = min(min(kItemRows, rows - q * kItemRows), max_rows - r0);
+                        it.pad = 0;
+                        items[idx] = it;
+                    }
+                }
+            }
+        }
+        if (tid == 0) {
+            int nact = 0, maxc = 0, nskip = 0, nbad = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                nact += s_act[q];
+                maxc = max(maxc, s_max[q]);
+                nskip += s_skip[q];
+                nbad += s_bad[q];
+            }
+            eoff[E] = total;
+            meta[kMetaNent] = nent;
+            meta[kMetaNblk] = gridDim.x;
+            meta[kMetaNr] = total;
+            meta[kMetaNt] = total / tm;
+            meta[kMetaNactive] = nact;
+            meta[kMetaMaxcnt] = maxc;
+            meta[kMetaNskip] = nskip;
+            meta[kMetaNbad] = nbad;
+            meta[kMetaTm] = tm;
+            meta[kMetaE] = E;
+            meta[kMetaK] = K;
+            if (items) ctl[0] = min(itotal, max_items);
+        }
+    }
+
+    // 3. placement of this block's entries (as k_place, offsets from LDS)
+    const int i = bstart + tid;
+    const bool inb = i < nent;
+    const int e = inb ? ids[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t same = __ballot(valid);
+    for (int p = 0; p < nbits; ++p) {
+        const bool bit = (e >> p) & 1;
+        const uint64_t bl = __ballot(bit);
+        same &= bit ? bl : ~bl;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(same & below);
+    const int count = __popcll(same);
+    if (valid && rank == 0) reinterpret_cast<unsigned char *>(wc)[e * 16 + wv] = (unsigned char)count;
+    __syncthreads();
+    if (valid) {
+        const int row = s_eoff[e] + s_before[e] + bytes_below(wc[e], wv) + rank;
+        pos[i] = row;
+        stok[row] = i / K;
+        sw[row] = w[i];
+    } else if (inb) {
+        pos[i] = -1;
+    }
+}
+
+int plan_fused_max_blocks() { return kFusedMaxBlocks; }
+
+hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E, int K, int tm,
+                             int nblk, int32_t *cnt, int32_t *eoff, int32_t *boff, int32_t *tiles,
+                             int32_t *stok, float *sw, int32_t *pos, int32_t *meta,
+                             void *ffn_scratch, int64_t max_items, int64_t max_rows, hipStream_t s)
+{
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    int32_t *ctl = static_cast<int32_t *>(ffn_scratch);
+    WorkItem *items = ffn_scratch ? reinterpret_cast<WorkItem *>(static_cast<char *>(ffn_scratch) +
+                                                                 kCtlBytes)
+                                  : nullptr;
+    hipLaunchKernelGGL(k_plan_fused, dim3(nblk), dim3(kPlanBlock), 0, s, ids, w, nent, E, K, tm,
+                       nbits, cnt, eoff, boff, tiles, stok, sw, pos, meta, ctl, items,
+                       (int)max_items, (int)max_rows);
+    return hipGetLastError();
+}
+
 hipError_t launch_hist(const int32_t *ids, int nent, int E, int nblk, int32_t *bcnt, hipStream_t s)
 {
     hipLaunchKernelGGL(k_hist, dim3(nblk), dim3(kPlanBlock), 0, s, ids, nent, E, bcnt);

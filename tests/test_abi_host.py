@@ -111,7 +111,9 @@ def test_forward_layout_is_consistent():
 
 def test_timer_rejects_bad_capacity():
     h = ctypes.c_void_p()
-    assert abi.lib().moe_timer_create(ctypes.byref(h), 0) == 1
+    assert abi.lib().moe_timer_create(ctypes.byref(h), 0, 1) == 1
+    assert abi.lib().moe_timer_create(ctypes.byref(h), 4, 0) == 1          # no stage selected
+    assert abi.lib().moe_timer_create(ctypes.byref(h), 4, 1 << 8) == 1     # no such stage
     assert abi.lib().moe_timer_destroy(None) == 1
 
 

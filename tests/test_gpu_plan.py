@@ -69,7 +69,10 @@ FUZZ = [
     (2048, 10, 512, 16, 0.25, 0.0, 9),     # tail-skipping shaped
     (4, 64, 64, 1, 0.0, 0.0, 10),          # K = E, duplicates allowed
     (200, 3, 1, 32, 0.5, 0.1, 11),         # one expert
-    (6000, 8, 256, 16, 0.0, 0.0, 12),      # many blocks
+    (6000, 8, 256, 16, 0.0, 0.0, 12),      # many blocks (three-launch path)
+    (4096, 8, 512, 16, 0.02, 0.01, 13),    # 32 blocks: largest single-launch plan
+    (32769, 1, 300, 16, 0.0, 0.0, 14),     # 33 blocks: smallest three-launch plan
+    (16384, 4, 1000, 8, 0.05, 0.0, 15),    # 64 blocks
 ]
 
 
