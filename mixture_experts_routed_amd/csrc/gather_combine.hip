@@ -64,44 +64,43 @@ __global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int
 }
 
 // out[t] = (((+0 + y[pos[tK]]) + y[pos[tK+1]]) + ...) in fp32, k ascending,
-// pos < 0 or >= max_rows skipped. vpr = float4 per row. Each lane owns up
-// to 4 float4 columns of a chunk of 256 float4, so the row chunk of every k
-// is one 4 KB wave-wide read.
+// pos < 0 or >= max_rows skipped. One workgroup per token; each lane owns the
+// float4 columns j = lane-in-block + 256*q. For a column, the rows of up to
+// kCombineGroup entries are loaded first (independent loads, all in flight),
+// then added in k order, so one memory latency covers a whole group.
+constexpr int kCombineGroup = 16;
+
 __global__ __launch_bounds__(256) void k_combine(const float4 *__restrict__ y, int64_t max_rows,
                                                  int vpr, const int32_t *__restrict__ pos, int T,
                                                  int K, float4 *__restrict__ out)
 {
-    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x;
     const int32_t *p = pos + (int64_t)t * K;
-    for (int j0 = 0; j0 < vpr; j0 += 4 * kWave) {
-        float4 acc[4];
+    for (int j = threadIdx.x; j < vpr; j += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k0 = 0; k0 < K; k0 += kCombineGroup) {
+            const int n = min(kCombineGroup, K - k0);
+            int row[kCombineGroup];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k = 0; k < K; ++k) {
-            const int r = p[k];
-            if (r < 0 || r >= max_rows) continue;
-            const float4 *src = y + (int64_t)r * vpr;
-            float4 v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = j0 + lane + q * kWave;
-                v[q] = (j < vpr) ? load_nt(src + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int u = 0; u < kCombineGroup; ++u) {
+                const int r = u < n ? p[k0 + u] : -1;  // wave-uniform: scalar loads
+                row[u] = (r >= 0 && r < max_rows) ? r : -1;
             }
+            float4 v[kCombineGroup];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[q].x += v[q].x;
-                acc[q].y += v[q].y;
-                acc[q].z += v[q].z;
-                acc[q].w += v[q].w;
-            }
-        }
+            for (int u = 0; u < kCombineGroup; ++u)
+                v[u] = row[u] >= 0 ? load_nt(y + (int64_t)row[u] * vpr + j)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = j0 + lane + q * kWave;
-            if (j < vpr) store_nt(out + (int64_t)t * vpr + j, acc[q]);
+            for (int u = 0; u < kCombineGroup; ++u)
+                if (row[u] >= 0) {
+                    acc.x += v[u].x;
+                    acc.y += v[u].y;
+                    acc.z += v[u].z;
+                    acc.w += v[u].w;
+                }
         }
+        store_nt(out + (int64_t)t * vpr + j, acc);
     }
 }
 
@@ -120,8 +119,7 @@ hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, 
                           int d, float *out, hipStream_t s)
 {
     const int vpr = d / 4;
-    const int blocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s,
                        reinterpret_cast<const float4 *>(y), max_rows, vpr, pos, T, K,
                        reinterpret_cast<float4 *>(out));
     return hipGetLastError();
