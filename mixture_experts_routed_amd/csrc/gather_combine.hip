@@ -64,19 +64,19 @@ __global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int
 }
 
 // out[t] = (((+0 + y[pos[tK]]) + y[pos[tK+1]]) + ...) in fp32, k ascending,
-// pos < 0 or >= max_rows skipped. One workgroup per token; each lane owns the
-// float4 columns j = lane-in-block + 256*q. For a column, the rows of up to
-// kCombineGroup entries are loaded first (independent loads, all in flight),
-// then added in k order, so one memory latency covers a whole group.
+// pos < 0 or >= max_rows skipped. One workgroup per token, sized to cover a
+// whole row (one float4 column per lane up to 1024 lanes); for a column, the
+// rows of up to kCombineGroup entries are loaded first (independent loads, all
+// in flight), then added in k order, so one memory latency covers a group.
 constexpr int kCombineGroup = 16;
 
-__global__ __launch_bounds__(256) void k_combine(const float4 *__restrict__ y, int64_t max_rows,
+__global__ __launch_bounds__(1024) void k_combine(const float4 *__restrict__ y, int64_t max_rows,
                                                  int vpr, const int32_t *__restrict__ pos, int T,
                                                  int K, float4 *__restrict__ out)
 {
     const int t = blockIdx.x;
     const int32_t *p = pos + (int64_t)t * K;
-    for (int j = threadIdx.x; j < vpr; j += 256) {
+    for (int j = threadIdx.x; j < vpr; j += blockDim.x) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int k0 = 0; k0 < K; k0 += kCombineGroup) {
             const int n = min(kCombineGroup, K - k0);
@@ -119,7 +119,8 @@ hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, 
                           int d, float *out, hipStream_t s)
 {
     const int vpr = d / 4;
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s,
+    const int threads = min(1024, (vpr + kWave - 1) / kWave * kWave);
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(threads), 0, s,
                        reinterpret_cast<const float4 *>(y), max_rows, vpr, pos, T, K,
                        reinterpret_cast<float4 *>(out));
     return hipGetLastError();
