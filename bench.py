@@ -172,6 +172,20 @@ def gateup_bytes(cfg, meta, T):
     return 2 * nactive * cfg.d * cfg.f * es + T * cfg.d * es + nr * cfg.f * es
 
 
+def stage_bytes(cfg, meta, T):
+    """Algorithmic HBM bytes of each HBM-bound kernel of one moe_forward call."""
+    es = 2 if cfg.dtype != "f32" else 4
+    nactive, nr, nent = int(meta[4]), int(meta[2]), int(meta[0])
+    nreal = nent - int(meta[6]) - int(meta[7])  # rows that hold an entry
+    return {
+        "gateup": gateup_bytes(cfg, meta, T),
+        # down: W_down of the active experts, h read, y written on real rows
+        "down": nactive * cfg.f * cfg.d * es + nr * cfg.f * es + nreal * cfg.d * 4,
+        # combine: y rows of every entry read, out written, pos read
+        "combine": nreal * cfg.d * 4 + T * cfg.d * 4 + nent * 4,
+    }
+
+
 def cpu_baseline(cfg, ids, w, x, seconds):
     import oracle
     from mixture_experts_routed_amd import synth
@@ -302,6 +316,8 @@ def main():
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},
         "stages_note": "per-kernel HIP events in a pass after the timed steps (events around "
                        "every kernel); the timed steps record the gate/up kernel only",
+        "stages_gbs": {k: round(b / (us[k] * 1e3), 1) for k, b in stage_bytes(cfg, meta, T).items()
+                       if us.get(k)},
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
         "roofline": {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
