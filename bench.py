@@ -294,6 +294,21 @@ def main():
     st_all = breakdown.read()
     breakdown.close()
 
+    # the router step before the layer (moe_route_topk on the first call's logits),
+    # timed on its own: it is not part of the layer step above
+    logits = torch.from_numpy(synth.router_logits(cfg, T)).to(dev)
+    r_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        abi.moe_route_topk(logits, T, E, K, r_ids, r_w)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        abi.moe_route_topk(logits, T, E, K, r_ids, r_w)
+    ev1.record()
+    torch.cuda.synchronize()
+    route_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+
     L = abi.moe_forward_layout(T, K, E, d, f, tm, abi.DTYPE_NAME[cfg.dtype])
     meta = ws[L.meta: L.meta + 4 * abi.META_N].view(torch.int32).cpu().numpy()
     us = {k: 1e3 * v[0] / max(v[1], 1) for k, v in st_all.items()}
@@ -313,6 +328,7 @@ def main():
                                "Zipf(1.1)-ranked per-expert bias"}[cfg.bias] +
                               ", softmax top-k renormalised"},
         "plan_us": us["hist"] + us["scan"] + us["place"],
+        "route_us": route_us,
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},
         "stages_note": "per-kernel HIP events in a pass after the timed steps (events around "
                        "every kernel); the timed steps record the gate/up kernel only",

@@ -87,6 +87,26 @@ enum moe_meta_field {
 #define MOE_MAX_EXPERTS 1024 /* one plan counter per expert in LDS ([P1] s.1 finding 1: 1024 counters) */
 #define MOE_PLAN_BLOCK 1024  /* entries per plan block (the page's block size) */
 
+#define MOE_ROUTE_MAX_K 64     /* picks per token of moe_route_topk (one wave lane each) */
+
+/*
+ * moe_route_topk -- the router step before the plan ([P1] s.1 finding 5 and
+ * s.3 name route_topk, which writes the routed ids). Per token: a softmax over
+ * the E logits, the K largest probabilities kept and renormalised to sum to
+ * one -- equivalently the K largest logits, weight k = exp(l_k - m) / sum over
+ * the K picks of exp(l_j - m), m the largest logit. Picks are in descending
+ * order; equal logits go to the lower expert id; NaN logits are never picked
+ * and if fewer than K logits are not NaN the remaining picks are id -1 with
+ * weight 0. fp32 arithmetic, exponentials summed in pick order.
+ * In:  logits [T][E] fp32. Out: ids [T*K] int32, w [T*K] fp32 (the inputs of
+ * moe_plan / moe_forward).
+ * Errors: MOE_EINVAL for T, E or K < 1, K > E, NULL/misaligned pointers;
+ * MOE_EUNSUPPORTED for E > MOE_MAX_EXPERTS or K > MOE_ROUTE_MAX_K; MOE_EHIP
+ * on a failed launch.
+ */
+int moe_route_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
+                   moe_stream_t stream);
+
 /* Host-side sizes of a plan. */
 typedef struct {
     int64_t nent;         /* T*K */

@@ -50,6 +50,7 @@ _lib = None
 P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
 _SIGS = {
+    "moe_route_topk": [P, I32, I32, I32, P, P, P],
     "moe_plan_sizes": [I32, I32, I32, I32, ctypes.POINTER(PlanSizes)],
     "moe_plan": [P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_gather": [P, I32, I32, I32, P, P, I64, P, P],
@@ -141,6 +142,11 @@ def moe_status_str(status: int) -> str:
 
 # ------------------------------------------------ entry points (same names) --
 
+def moe_route_topk(logits, T, E, K, ids, w, stream=None):
+    _check("moe_route_topk", lib().moe_route_topk(_dev(logits, "logits"), T, E, K, _dev(ids, "ids"),
+                                                  _dev(w, "w"), _stream(stream)))
+
+
 def moe_plan(ids, w, T, K, E, tm, cnt, eoff, tiles, stok, sw, pos, boff, meta, scratch,
              stream=None):
     _check("moe_plan", lib().moe_plan(
@@ -221,6 +227,15 @@ class Timer:
 
 def _empty(n, dtype, device):
     return torch.empty(int(max(n, 1)), dtype=dtype, device=device)
+
+
+def route(logits, K: int, stream=None):
+    """Router on GPU logits [T, E] fp32: returns (ids [T, K] int32, w [T, K] fp32)."""
+    T, E = logits.shape
+    ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    moe_route_topk(logits, T, E, K, ids, w, stream)
+    return ids, w
 
 
 def plan(ids, w, E: int, tm: int = 16, stream=None) -> dict:

@@ -272,6 +272,18 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
 
 extern "C" {
 
+int moe_route_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
+                   moe_stream_t stream)
+{
+    if (T < 1 || E < 1 || K < 1 || K > E) return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS || K > MOE_ROUTE_MAX_K) return MOE_EUNSUPPORTED;
+    if ((int64_t)T * E > kI32Max * 4 || (int64_t)T * K > kI32Max) return MOE_EINVAL;
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4)) return MOE_EINVAL;
+    if (moe::launch_route_topk(logits, T, E, K, ids, w, as_stream(stream)) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
 int moe_plan_sizes(int T, int K, int E, int tm, moe_plan_sizes_t *out)
 {
     if (!out) return MOE_EINVAL;

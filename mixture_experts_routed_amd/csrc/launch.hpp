@@ -25,6 +25,10 @@ hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E
                              int32_t *stok, float *sw, int32_t *pos, int32_t *meta,
                              void *ffn_scratch, int64_t max_items, int64_t max_rows, hipStream_t s);
 
+// ---- router ----
+hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
+                             hipStream_t s);
+
 // ---- gather and combine ----
 hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int32_t *stok,
                          const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s);

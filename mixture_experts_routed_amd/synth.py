@@ -139,6 +139,14 @@ def routing(cfg: Config, T: int | None = None):
     return order.astype(np.int32), w.astype(np.float32)
 
 
+def router_logits(cfg: Config, T: int | None = None) -> np.ndarray:
+    """Router logits as the router GEMM would hand them over: fp32 [T, E]
+    (N(0,1) + the config's per-expert bias, rounded from fp64)."""
+    T = cfg.T if T is None else T
+    logits = rng(cfg.seed, TAG_LOGITS).standard_normal((T, cfg.E)) + router_bias(cfg)[None, :]
+    return logits.astype(np.float32)
+
+
 def activations(cfg: Config, T: int | None = None) -> np.ndarray:
     """Token activations x [T, d] in the config's element type (raw storage)."""
     T = cfg.T if T is None else T

@@ -77,6 +77,8 @@ def lib():
                                          P, P, i32]
         L.oracle_dense_masked.restype = i32
         L.oracle_dense_masked.argtypes = [P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, P]
+        L.oracle_route_topk.restype = i32
+        L.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
         L.oracle_combine_f32.restype = None
         L.oracle_combine_f32.argtypes = [P, P, i64, i32, i32, P]
         _lib = L
@@ -242,3 +244,17 @@ def combine_f32(Y: np.ndarray, pos: np.ndarray, T: int, K: int) -> np.ndarray:
     out = np.empty((T, d), np.float32)
     lib().oracle_combine_f32(_p(Y), _p(pos), T, K, d, _p(out))
     return out
+
+
+# ----------------------------------------------------------------- router --
+
+def route_topk(logits: np.ndarray, K: int):
+    """ids int32 [T, K] (descending logit, ties to the lower id, NaN never picked, -1 if
+    fewer than K finite picks) and renormalised softmax weights float64 [T, K]."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    if lib().oracle_route_topk(_p(logits), T, E, K, _p(ids), _p(w)) != 0:
+        raise ValueError("oracle_route_topk: bad arguments")
+    return ids, w

@@ -467,3 +467,46 @@ void oracle_combine_f32(const float *Y, const int32_t *pos, int64_t T, int K, in
             out[t * d + c] = acc;
         }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Router: [P1] s.1 finding 5 and s.3 name the kernel that writes the routed  */
+/* ids (route_topk); the workload description fixes what it computes: a      */
+/* softmax over the E router logits, the K largest probabilities kept and     */
+/* renormalised to sum to one. Since softmax is monotone, the K largest       */
+/* probabilities are the K largest logits, and the renormalised weight of     */
+/* pick k is exp(l_k - m) / sum over the K picks of exp(l_j - m), m = the     */
+/* largest logit (the full softmax denominator cancels).                      */
+/* Order: descending logit, equal logits by ascending expert id. NaN logits   */
+/* are never picked; if fewer than K logits are not NaN, the remaining picks  */
+/* are id -1 with weight 0.                                                   */
+/* ------------------------------------------------------------------------- */
+int oracle_route_topk(const float *logits, int64_t T, int E, int K, int32_t *ids, double *w)
+{
+    if (T < 1 || E < 1 || K < 1)
+        return -1;
+    char *taken = (char *)malloc((size_t)E);
+    if (!taken)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + (size_t)t * E;
+        for (int e = 0; e < E; ++e) taken[e] = isnan(l[e]) ? 1 : 0;
+        int n = 0;
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)  /* first index wins ties */
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            ids[t * K + k] = best;
+            if (best >= 0) {
+                taken[best] = 1;
+                n++;
+            }
+        }
+        double m = n > 0 ? (double)l[ids[t * K]] : 0.0, sum = 0.0;
+        for (int k = 0; k < n; ++k) sum += exp((double)l[ids[t * K + k]] - m);
+        for (int k = 0; k < K; ++k)
+            w[t * K + k] = k < n ? exp((double)l[ids[t * K + k]] - m) / sum : 0.0;
+    }
+    free(taken);
+    return 0;
+}

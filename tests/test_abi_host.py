@@ -128,3 +128,12 @@ def test_no_device_gives_ehip_without_crash():
     # valid arguments, fake addresses, no GPU: the launch fails and the call reports it
     L = abi.lib()
     assert L.moe_combine(A, 64, A, 4, 2, 16, A, None) == 3
+
+
+def test_route_rejects_bad_arguments():
+    L = abi.lib()
+    assert L.moe_route_topk(A, 4, 8, 9, A, A, None) == 1      # K > E
+    assert L.moe_route_topk(A, 0, 8, 2, A, A, None) == 1      # T < 1
+    assert L.moe_route_topk(A, 4, 2048, 8, A, A, None) == 2   # E too large
+    assert L.moe_route_topk(A, 4, 512, 65, A, A, None) == 2   # K too large
+    assert L.moe_route_topk(A + 2, 4, 8, 2, A, A, None) == 1  # misaligned
