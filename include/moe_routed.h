@@ -165,9 +165,27 @@ int moe_gather(const void *x, int dtype, int T, int d, const int32_t *stok, cons
 
 /*
  * moe_ffn_scratch_bytes -- host only: scratch moe_expert_ffn needs for a plan
- * of at most max_rows rows over E experts with tile tm.
+ * of at most max_rows rows over E experts with tile tm, hidden size d,
+ * intermediate size f and element type dtype (the work list, plus fp32
+ * partial sums when a projection is split along its reduction, see
+ * moe_ffn_splits).
+ * Errors: MOE_EINVAL for NULL bytes, E/tm/max_rows < 1, d or f not positive
+ * multiples of 8, bad dtype; MOE_EUNSUPPORTED for E > MOE_MAX_EXPERTS.
  */
-int moe_ffn_scratch_bytes(int E, int tm, int64_t max_rows, size_t *bytes);
+int moe_ffn_scratch_bytes(int E, int d, int f, int tm, int64_t max_rows, int dtype,
+                          size_t *bytes);
+
+/*
+ * moe_ffn_splits -- host only: into how many reduction ranges moe_expert_ffn
+ * (and moe_forward) split the gate/up projection (over d) and the down
+ * projection (over f) for these sizes. A projection is split when the bound on
+ * its work items is too small to occupy the GPU (decode-sized batches); the
+ * partial sums are then added in a fixed order, so results stay deterministic
+ * run to run but differ in rounding from the unsplit order. Same argument
+ * checks as moe_ffn_scratch_bytes.
+ */
+int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *split_gateup,
+                   int *split_down);
 
 /*
  * moe_expert_ffn -- the grouped expert FFN over the expert-sorted rows

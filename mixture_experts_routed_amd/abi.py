@@ -54,7 +54,9 @@ _SIGS = {
     "moe_plan_sizes": [I32, I32, I32, I32, ctypes.POINTER(PlanSizes)],
     "moe_plan": [P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_gather": [P, I32, I32, I32, P, P, I64, P, P],
-    "moe_ffn_scratch_bytes": [I32, I32, I64, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_ffn_scratch_bytes": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_ffn_splits": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int),
+                       ctypes.POINTER(ctypes.c_int)],
     "moe_expert_ffn": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ, P],
     "moe_combine": [P, I64, P, I32, I32, I32, P, P],
     "moe_forward_workspace": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -117,10 +119,19 @@ def moe_plan_sizes(T: int, K: int, E: int, tm: int) -> PlanSizes:
     return z
 
 
-def moe_ffn_scratch_bytes(E: int, tm: int, max_rows: int) -> int:
+def moe_ffn_scratch_bytes(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int) -> int:
     v = ctypes.c_size_t()
-    _check("moe_ffn_scratch_bytes", lib().moe_ffn_scratch_bytes(E, tm, max_rows, ctypes.byref(v)))
+    _check("moe_ffn_scratch_bytes",
+           lib().moe_ffn_scratch_bytes(E, d, f, tm, max_rows, dtype, ctypes.byref(v)))
     return v.value
+
+
+def moe_ffn_splits(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int):
+    """(gate/up splits, down splits) of the reduction for these sizes."""
+    a, b = ctypes.c_int(), ctypes.c_int()
+    _check("moe_ffn_splits",
+           lib().moe_ffn_splits(E, d, f, tm, max_rows, dtype, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def moe_forward_workspace(T, K, E, d, f, tm, dtype: int) -> int:

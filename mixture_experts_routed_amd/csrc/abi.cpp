@@ -51,11 +51,15 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
         return MOE_EINVAL;
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
     if (max_rows * (int64_t)(d > f ? d : f) > ((int64_t)1 << 40)) return MOE_EINVAL;
+    // one expert matrix is addressed by one buffer descriptor (32-bit offsets)
+    if ((int64_t)d * f * elem_bytes(dtype) > ((int64_t)1 << 31)) return MOE_EINVAL;
     if (!aligned(xs, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) ||
         !aligned(h, 16) || !aligned(y, 16) || !aligned(eoff, 4) || !aligned(stok, 4) ||
         !aligned(sw, 4) || !aligned(meta, 4) || !aligned(scratch, 16))
         return MOE_EINVAL;
-    if (scratch_bytes < moe::ffn_scratch_bytes(E, tm, max_rows)) return MOE_EINVAL;
+    const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
+    if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max) return MOE_EINVAL;
+    if (scratch_bytes < z.scratch_bytes) return MOE_EINVAL;
     return MOE_OK;
 }
 
@@ -170,23 +174,23 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
     const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                              y, scratch, scratch_bytes);
     if (rc != MOE_OK) return rc;
-    const int64_t max_items = moe::ffn_max_items(E, tm, max_rows);
+    const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
     if (!have_items) {
         Rec r(tmr, s, MOE_STAGE_WORKLIST);
-        if (moe::launch_worklist(eoff, E, max_rows, scratch, max_items, s) != hipSuccess)
+        if (moe::launch_worklist(eoff, E, max_rows, scratch, z.max_items, s) != hipSuccess)
             return MOE_EHIP;
     }
     {
         Rec r(tmr, s, MOE_STAGE_GATEUP);
         const hipError_t e =
-            x ? moe::launch_gateup_gathered(dtype, x, T, stok, wg, wu, d, f, scratch, max_items, h,
+            x ? moe::launch_gateup_gathered(z, dtype, x, T, stok, wg, wu, d, f, meta, scratch, h,
                                             s)
-              : moe::launch_gateup(dtype, xs, wg, wu, d, f, scratch, max_items, h, s);
+              : moe::launch_gateup(z, dtype, xs, wg, wu, d, f, meta, scratch, h, s);
         if (e != hipSuccess) return MOE_EHIP;
     }
     {
         Rec r(tmr, s, MOE_STAGE_DOWN);
-        if (moe::launch_down(dtype, h, wd, d, f, stok, sw, scratch, max_items, y, s) != hipSuccess)
+        if (moe::launch_down(z, dtype, h, wd, d, f, stok, sw, meta, scratch, y, s) != hipSuccess)
             return MOE_EHIP;
     }
     return MOE_OK;
@@ -228,7 +232,7 @@ int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forwar
     L->xs = take(R * d * es);
     L->h = take(R * f * es);
     L->y = take(R * d * 4);
-    L->ffn_scratch = take(moe::ffn_scratch_bytes(E, tm, z->max_rows));
+    L->ffn_scratch = take(moe::ffn_shape(E, tm, z->max_rows, d, f, dtype).scratch_bytes);
     L->total = o;
     return MOE_OK;
 }
@@ -262,7 +266,7 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     }
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
-                  moe::ffn_scratch_bytes(E, tm, z.max_rows), s, tmr, items,
+                  moe::ffn_shape(E, tm, z.max_rows, d, f, dtype).scratch_bytes, s, tmr, items,
                   fused_gather ? x : nullptr, T);
     if (rc != MOE_OK) return rc;
     return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);
@@ -304,11 +308,27 @@ int moe_gather(const void *x, int dtype, int T, int d, const int32_t *stok, cons
     return gather_impl(x, dtype, T, d, stok, meta, max_rows, xs, as_stream(stream), nullptr);
 }
 
-int moe_ffn_scratch_bytes(int E, int tm, int64_t max_rows, size_t *bytes)
+int moe_ffn_scratch_bytes(int E, int d, int f, int tm, int64_t max_rows, int dtype,
+                          size_t *bytes)
 {
-    if (!bytes || E < 1 || tm < 1 || max_rows < 1 || max_rows > kI32Max - 1024) return MOE_EINVAL;
+    if (!bytes || E < 1 || tm < 1 || max_rows < 1 || max_rows > kI32Max - 1024 ||
+        !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 || f % 8)
+        return MOE_EINVAL;
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
-    *bytes = moe::ffn_scratch_bytes(E, tm, max_rows);
+    *bytes = moe::ffn_shape(E, tm, max_rows, d, f, dtype).scratch_bytes;
+    return MOE_OK;
+}
+
+int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *split_gateup,
+                   int *split_down)
+{
+    if (!split_gateup || !split_down || E < 1 || tm < 1 || max_rows < 1 ||
+        max_rows > kI32Max - 1024 || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 || f % 8)
+        return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
+    *split_gateup = z.split_gu;
+    *split_down = z.split_dn;
     return MOE_OK;
 }
 

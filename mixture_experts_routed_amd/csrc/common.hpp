@@ -26,12 +26,25 @@ constexpr int kItemRows = 64;
 constexpr size_t kCtlBytes = 256;
 
 // A work item of the grouped FFN: one expert's run of at most kItemRows rows.
+// `run` groups consecutive items of one expert whose workgroups share the
+// expert's weight tile: run length (1, 2 or 4) | (index in the run << 8).
 struct WorkItem {
     int32_t expert;
     int32_t row0;
     int32_t nrows;
-    int32_t pad;
+    int32_t run;
 };
+
+// Run of item q of an expert's n items: runs of 4 first, then one run of 2 if
+// at least 2 items remain, else single items.
+__host__ __device__ inline int32_t item_run(int q, int n)
+{
+    const int n4 = n & ~3;
+    if (q < n4) return 4 | ((q & 3) << 8);
+    const int q2 = q - n4;
+    if (n - n4 >= 2 && q2 < 2) return 2 | (q2 << 8);
+    return 1;
+}
 
 __device__ __forceinline__ int wave_sum(int v)
 {

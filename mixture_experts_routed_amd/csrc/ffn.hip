@@ -12,20 +12,29 @@
 // Design (MI355X): at 512 experts x ~48 rows each, the weights (6 GB at the
 // prefill shape) are streamed once and every weight element meets only a few
 // dozen rows, so these GEMMs are bound by HBM, not by the matrix cores.
-//  * Work unit = one wavefront: (work item, 64-column slice of the output).
-//    A work item is one expert's run of up to 64 rows, so each expert's
-//    weights are read from HBM once (experts with more rows get more items).
+//  * Work list: each expert's rows cut into items of <= 64 rows. A workgroup
+//    (4 wavefronts) covers 4 x 64 output rows-by-columns "cells" of one
+//    expert; per item there are ceil(N / (4 slices)) workgroups, so the grid
+//    is (items x column groups x K-splits) whatever the shape of the cells.
+//  * Wide cells (an expert with a single item, the common case): the 4
+//    wavefronts share the item's rows (A tile through LDS) and each streams its
+//    own column slice of the weights straight into registers.
+//  * Tall cells (runs of 2 or 4 items of one expert): the wavefronts take
+//    different row blocks of the same column slice(s) and share the weight
+//    tile through LDS, so such an expert's weights are read once per 256
+//    (or 128) rows instead of once per 64 rows.
+//  * Split-K when the host-side bound on work items is too small to fill the
+//    256 CUs (decode-sized batches): each split accumulates a K range into an
+//    fp32 partial plane, and a reduce kernel adds the planes in split order
+//    and applies the epilogue (SwiGLU, or the router weight).
 //  * Matrix cores: v_mfma_f32_16x16x32_{f16,bf16} (v_mfma_f32_16x16x4_f32 for
 //    fp32). The weights are row-major [K][N] (N contiguous) but an MFMA lane
 //    needs 8 consecutive K of one column. Each lane loads 8 K-rows x 4
 //    columns (8-byte loads; 16 lanes cover one 128-byte row segment) and
 //    transposes the 8x4 block in registers into 4 B-fragments: fragment c
 //    feeds MFMA c, whose 16 columns are the logical columns 4*j + c of the
-//    slice. No LDS staging, no repacking of the weights by the caller.
-//  * A operand rows (16-byte loads of 8 K) come straight from global memory;
-//    the 12-40 waves that share an expert's rows sit on one XCD (see
-//    xcd_logical_block), so they hit that XCD's L2.
-//  * Loads of K-step s+1 are issued before the MFMAs of step s.
+//    slice. No repacking of the weights by the caller.
+//  * Loads of K-step s+S-1 are issued before the MFMAs of step s.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,18 +42,67 @@ namespace moe {
 
 constexpr int kMT = kItemRows / 16;     // 16-row m-tiles per work item
 constexpr int kWavesPerBlock = 4;
+constexpr int kNpl = 4;                 // columns per lane and B stream
 
 int ffn_rows_per_item() { return kItemRows; }
 
+// Items are ceil(cnt_e / 64) per active expert, so their number is at most
+// (active experts) + (entries beyond one per active expert) / 64; with rows
+// padded to tm this is bounded from max_rows as below.
 int64_t ffn_max_items(int E, int tm, int64_t max_rows)
 {
     const int64_t per_tile = (max_rows + tm - 1) / tm;
     return max_rows / kItemRows + 1 + (E < per_tile ? E : per_tile);
 }
 
-size_t ffn_scratch_bytes(int E, int tm, int64_t max_rows)
+// ---- host-side shape of the two grouped GEMMs ------------------------------
+namespace {
+
+// columns of one workgroup's 4 slices: gate/up 4 x 64, down 4 x 128
+int group_cols(bool gateup) { return kWavesPerBlock * (gateup ? 16 * kNpl : 32 * kNpl); }
+
+// Split-K is used when fewer than this many (item, column group) cells exist
+// at most: about two workgroups per CU.
+constexpr int64_t kTargetCells = 512;
+constexpr int kMinStepsPerSplit = 8;
+constexpr int kMaxSplit = 8;
+
+void split_for(int64_t cells, int Kd, int kstep, int *nsplit, int *steps)
 {
-    return kCtlBytes + (size_t)ffn_max_items(E, tm, max_rows) * sizeof(WorkItem);
+    const int nsteps = (Kd + kstep - 1) / kstep;
+    int s = 1;
+    if (cells < kTargetCells) s = (int)((kTargetCells + cells - 1) / cells);
+    s = s < kMaxSplit ? s : kMaxSplit;
+    const int smax = nsteps / kMinStepsPerSplit > 1 ? nsteps / kMinStepsPerSplit : 1;
+    s = s < smax ? s : smax;
+    const int per = (nsteps + s - 1) / s;
+    *steps = per;
+    *nsplit = (nsteps + per - 1) / per;  // every split has >= 1 step
+}
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
+{
+    FfnShape z;
+    z.max_items = ffn_max_items(E, tm, max_rows);
+    z.max_rows = max_rows;
+    const int kstep = dtype == 0 ? 16 : 32;
+    const int64_t gs_gu = (f + group_cols(true) - 1) / group_cols(true);
+    const int64_t gs_dn = (d + group_cols(false) - 1) / group_cols(false);
+    split_for(z.max_items * gs_gu, d, kstep, &z.split_gu, &z.steps_gu);
+    split_for(z.max_items * gs_dn, f, kstep, &z.split_dn, &z.steps_dn);
+    z.blocks_gu = (z.max_items * gs_gu * z.split_gu + 7) / 8 * 8;
+    z.blocks_dn = (z.max_items * gs_dn * z.split_dn + 7) / 8 * 8;
+    z.plane_gu = max_rows * 2 * (int64_t)f;
+    z.plane_dn = max_rows * (int64_t)d;
+    const size_t pg = z.split_gu > 1 ? (size_t)z.split_gu * z.plane_gu * 4 : 0;
+    const size_t pd = z.split_dn > 1 ? (size_t)z.split_dn * z.plane_dn * 4 : 0;
+    z.part_offset = round256(kCtlBytes + (size_t)z.max_items * sizeof(WorkItem));
+    z.scratch_bytes = z.part_offset + (pg > pd ? pg : pd);
+    return z;
 }
 
 // Work list: each expert's row range [eoff[e], eoff[e+1]) cut into items of at
@@ -83,7 +141,7 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
             it.expert = tid;
             it.row0 = r0 + q * kItemRows;
             it.nrows = min(kItemRows, rows - q * kItemRows);
-            it.pad = 0;
+            it.run = item_run(q, n);
             items[idx] = it;
         }
     }
@@ -93,7 +151,8 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
 // ---- raw buffer loads -----------------------------------------------------
 // A buffer resource covering exactly one operand range: loads past its end
 // return zeros without touching memory (range-checked by the hardware), which
-// zero-fills the K tail of the weights and the rows past a work item's end.
+// zero-fills the K tail of the weights, the rows past a work item's end and
+// the steps past the end of a K split.
 // Word 3 = 0x00020000: raw (untyped) buffer on gfx9-family GPUs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -172,17 +231,23 @@ template <> struct Elt<float> {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// 16-bit B operand: 8 consecutive K-rows of NPL columns each (row i = K-value
-// i). Column c of them, as one MFMA operand (element i = K-row i).
-__device__ __forceinline__ uint4 column_of_rows(const uint2 (&r)[8], int c)
+// 16-bit B operand: RP consecutive K-rows of 4 columns each (row i = K-value
+// i). Column c of them as RP/2 words of an MFMA operand (element i = K-row i).
+template <int RP>
+__device__ __forceinline__ void column_of_rows(const uint2 (&r)[RP], int c, uint32_t (&o)[RP / 2])
 {
-    uint32_t o[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < RP / 2; ++p) {
         const uint32_t lo = (c < 2) ? r[2 * p].x : r[2 * p].y;
         const uint32_t hi = (c < 2) ? r[2 * p + 1].x : r[2 * p + 1].y;
         o[p] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
     }
+}
+
+__device__ __forceinline__ uint4 column_of_rows(const uint2 (&r)[8], int c)
+{
+    uint32_t o[4];
+    column_of_rows<8>(r, c, o);
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -196,45 +261,152 @@ __device__ __forceinline__ float lanef(const uint4 &v, int q)
     return __builtin_bit_cast(float, word(v, q));
 }
 
-// Pipeline depth for NMT m-tiles: stage = 32 B-operand + 4 A-operand VGPRs,
-// accumulators = 32*NMT VGPRs; S stages + accumulators stay <= ~232.
+__device__ __forceinline__ uint4 mask4(uint4 v, uint32_t m)
+{
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Arguments of one grouped GEMM launch.
+//   gate/up: A = xs [rows][d] (or x [a_rows][d] when GATHERED), B0 = W_gate,
+//            B1 = W_up [E][d][f], out = h [rows][f] (type T).
+//   down:    A = h [rows][f], B0 = W_down [E][f][d], out = y [rows][d] (fp32),
+//            stok / sw for the epilogue.
+// With nsplit > 1 the epilogue instead writes fp32 partial sums: split s at
+// part + s * plane, row r at r * 2N (gate: columns [0, N), up: [N, 2N)) or at
+// r * N (down, without the router weight).
+// The item count and the work items are separate __restrict__ kernel
+// arguments: provably read-only, they are fetched with scalar loads.
+struct GemmArgs {
+    const void *A;
+    const void *B0;
+    const void *B1;
+    const int32_t *stok;
+    const float *sw;
+    void *out;
+    float *part;
+    int64_t plane;
+    int a_rows;
+    int Kd, N;
+    int nsplit;       // K splits per (item, column group)
+    int split_steps;  // K-steps per split
+};
+
+// Epilogue of one wavefront: acc[m][mt][c][r] is the output at row
+// 16*mt + 4*kg + r of item `it` and column col + c (+ HALF for m = 1 of the
+// down projection). rinfo[l] = (router weight, token) of the item's row l.
+template <typename T, bool GATEUP, int NMT>
+__device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &it, int col, int kg,
+                                            const float4_t (&acc)[2][NMT][kNpl],
+                                            const float2 *__restrict__ rinfo, int split)
+{
+    constexpr int ES = sizeof(T);
+    constexpr int HALF = GATEUP ? 0 : 16 * kNpl;
+    const int N = p.N;
+    if (col >= N) return;
+    const bool partial = p.nsplit > 1;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = 16 * mt + 4 * kg + r;
+            if (rl >= it.nrows) continue;
+            const int64_t row = it.row0 + rl;
+            if constexpr (GATEUP) {
+                if (partial) {
+                    float *P = p.part + split * p.plane + row * 2 * N + col;
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        *reinterpret_cast<float4 *>(P + m * N) =
+                            make_float4(acc[m][mt][0][r], acc[m][mt][1][r], acc[m][mt][2][r],
+                                        acc[m][mt][3][r]);
+                    continue;
+                }
+                float hv[kNpl];
+#pragma unroll
+                for (int c = 0; c < kNpl; ++c) hv[c] = silu(acc[0][mt][c][r]) * acc[1][mt][c][r];
+                T *H = static_cast<T *>(p.out) + row * N + col;
+                if constexpr (ES == 2)
+                    store_nt(reinterpret_cast<uint2 *>(H),
+                             make_uint2(Elt<T>::pack2(hv[0], hv[1]), Elt<T>::pack2(hv[2], hv[3])));
+                else
+                    store_nt(reinterpret_cast<float4 *>(H), make_float4(hv[0], hv[1], hv[2], hv[3]));
+            } else {
+                const float2 ri = rinfo[rl];
+                if (__float_as_int(ri.y) < 0) continue;  // pad rows are never combined
+                const float g = partial ? 1.0f : ri.x;
+                float *Y = partial ? p.part + split * p.plane + row * N + col
+                                   : static_cast<float *>(p.out) + row * N + col;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (col + m * HALF >= N) continue;
+                    const float4 v = make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
+                                                 g * acc[m][mt][2][r], g * acc[m][mt][3][r]);
+                    if (partial)
+                        *reinterpret_cast<float4 *>(Y + m * HALF) = v;
+                    else
+                        store_nt(reinterpret_cast<float4 *>(Y + m * HALF), v);
+                }
+            }
+        }
+    }
+}
+
+// (router weight, token) of the item's rows for the down epilogue
+__device__ __forceinline__ void load_rinfo(const GemmArgs &p, const WorkItem &it, int l,
+                                           float2 *__restrict__ rinfo)
+{
+    const bool ok = l < it.nrows;
+    const int64_t r = it.row0 + (ok ? l : 0);
+    rinfo[l] = make_float2(ok ? p.sw[r] : 0.f, __int_as_float(ok ? p.stok[r] : -1));
+}
+
+// Pipeline depth of the wide cells for NMT m-tiles: stage = 32 B-operand + 4
+// A-operand VGPRs, accumulators = 32*NMT VGPRs; S stages + accumulators stay
+// <= ~232.
 constexpr int stages_for(int nmt) { return nmt >= 4 ? 2 : nmt == 3 ? 3 : nmt == 2 ? 4 : 5; }
 
 // Shared A tile of one K-step: 64 rows x 32 K (16-bit) or 64 rows x 16 K
 // (fp32), 64 bytes per row, double-buffered: 2 x 4 KB of LDS per workgroup.
-constexpr int kATileBytes = kItemRows * 64;
+constexpr int kATileU4 = kItemRows * 64 / 16;
+// Shared B tile of the tall cells: per column slice 2 matrices x 64 lanes x
+// 64 bytes (4 fragments of 16 bytes per lane), double-buffered.
+constexpr int tall_buf_u4(int nslices) { return nslices * 2 * 64 * 4; }
+constexpr int kLdsU4 = 2 * tall_buf_u4(2) > 2 * kATileU4 ? 2 * tall_buf_u4(2) : 2 * kATileU4;
 
-// A workgroup of 4 wavefronts computes one work item (<= 64 rows) against 4
-// adjacent column slices of 16*NPL columns, one slice per wavefront.
+// Wide cells: a workgroup of 4 wavefronts computes one work item (<= 64 rows)
+// against 4 adjacent column slices of 16*kNpl columns, one per wavefront.
 //  * A (the item's rows) is shared: per K-step each wavefront loads 16 rows x
 //    64 bytes (one 16-byte load per lane) into registers, writes them to an LDS
 //    slot, and after one barrier every wavefront reads its MFMA A-fragments
 //    from LDS. One copy of A per workgroup instead of one per wavefront.
 //  * B (the weights) is private to each wavefront: lane l supplies MFMA column
-//    (l & 15) and K-group (l >> 4); it loads KR K-rows x NPL columns of each
-//    weight matrix per step (16 lanes cover one 16*NPL-column row segment) and
+//    (l & 15) and K-group (l >> 4); it loads KR K-rows x kNpl columns of each
+//    weight matrix per step (16 lanes cover one 16*kNpl-column row segment) and
 //    transposes them in registers, so MFMA c produces the logical columns
-//    NPL*j + c, j = 0..15.
+//    kNpl*j + c, j = 0..15.
 //  * S-stage register ring: the loads of step s+S-1 are issued before the
 //    MFMAs of step s; the loop body is straight-line code, so they stay in
 //    flight. The per-step barrier keeps the 4 wavefronts in step, so together
 //    they read 4 adjacent row segments of every weight row.
 // GATHERED (gate/up only): A is the token activation x [a_rows][Kd] and row r
 // of the item reads x[stok[r]] -- the gather fused into the A-tile loads.
-template <typename T, bool GATEUP, bool GATHERED, int NPL, int NMT>
-__device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
-                                          const T *__restrict__ B0,
-                                          const T *__restrict__ B1, int Kd, int N, WorkItem it,
-                                          int slice, const int32_t *__restrict__ stok,
-                                          const float *__restrict__ sw, void *__restrict__ out,
-                                          uint4 *__restrict__ a_lds, float2 *__restrict__ rinfo)
+// The K range is [kb, ke) (a split of the reduction, or all of it).
+template <typename T, bool GATEUP, bool GATHERED, int NMT>
+__device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it, int slice,
+                                           int kb, int ke, int split, uint4 *__restrict__ a_lds,
+                                           float2 *__restrict__ rinfo)
 {
+    constexpr int NPL = kNpl;
     constexpr int ES = sizeof(T);
     constexpr int KR = Elt<T>::KR;
     constexpr int KSTEP = 4 * KR;
-    constexpr int NMAT = 2;       // two B streams (see above)
+    constexpr int NMAT = 2;       // two B streams (see below)
     constexpr int LB = NPL * ES;  // bytes per lane per row
     typedef typename Ld<LB>::type RowT;
+    const T *A = static_cast<const T *>(p.A);
+    const T *B0 = static_cast<const T *>(p.B0);
+    const T *B1 = static_cast<const T *>(p.B1);
+    const int Kd = p.Kd, N = p.N;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -247,15 +419,16 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
     const int col = slice * SW + NPL * nq;
     const bool slice_ok = slice * SW < N;  // wave-uniform
 
-    // operand ranges: this expert's weight matrices (empty for a surplus
+    // operand ranges: this expert's weight rows [kb, ke) (empty for a surplus
     // slice: its loads return zeros without memory traffic), this item's rows
-    const size_t wofs = (size_t)it.expert * Kd * N;
-    const uint32_t wbytes = slice_ok ? (uint32_t)((size_t)Kd * N * ES) : 0u;
+    const size_t wofs = (size_t)it.expert * Kd * N + (size_t)kb * N;
+    const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
+    const uint32_t wbytes = slice_ok ? kbytes : 0u;
     const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + wofs, wbytes);
-    // (Kd*N >= 64 >= HALF, so the second range never underflows; readfirstlane
-    // keeps the wave-uniform value in an SGPR)
+    // ((ke-kb)*N >= 8*8 >= HALF, so the second range never underflows;
+    // readfirstlane keeps the wave-uniform value in an SGPR)
     const uint32_t wbytes1 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(slice_ok ? (uint32_t)((size_t)Kd * N * ES - (size_t)HALF * ES) : 0u));
+        (int)(slice_ok ? kbytes - (uint32_t)(HALF * ES) : 0u));
     const __amdgpu_buffer_rsrc_t rb1 =
         GATEUP ? make_rsrc(B1 + wofs, wbytes) : make_rsrc(B0 + wofs + HALF, wbytes1);
     const uint32_t rowb = (uint32_t)N * ES;  // bytes per weight row
@@ -267,23 +440,17 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
     if constexpr (GATHERED) {
         // all of x (< 2 GiB, checked by the host); a pad row (token -1) or a
         // row past the item starts at 2^31, outside the range: it reads zeros
-        ra = make_rsrc(A, (uint32_t)((size_t)a_rows * Kd * ES));
-        const int t = arow < it.nrows ? stok[it.row0 + arow] : -1;
-        va0 = (unsigned)t < (unsigned)a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
+        ra = make_rsrc(A, (uint32_t)((size_t)p.a_rows * Kd * ES));
+        const int t = arow < it.nrows ? p.stok[it.row0 + arow] : -1;
+        va0 = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
     } else {
         ra = make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
         va0 = (uint32_t)arow * (uint32_t)Kd * ES;
     }
 
-    if constexpr (!GATEUP) {
-        // router weight and token of the item's rows for the epilogue (made
-        // visible to all wavefronts by the barriers of the K loop)
-        if (tid < kItemRows) {
-            const bool ok = tid < it.nrows;
-            const int64_t r = it.row0 + (ok ? tid : 0);
-            rinfo[tid] = make_float2(ok ? sw[r] : 0.f, __int_as_float(ok ? stok[r] : -1));
-        }
-    }
+    // made visible to all wavefronts by the barriers of the K loop
+    if constexpr (!GATEUP)
+        if (tid < kItemRows) load_rinfo(p, it, tid, rinfo);
 
     float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
@@ -299,20 +466,19 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
     };
     auto load = [&](Stage &st, int k0) {
         const int kk = k0 + KR * kg;
-        const uint32_t vb = vcol + (uint32_t)kk * rowb;
+        const uint32_t vb = vcol + (uint32_t)(kk - kb) * rowb;
 #pragma unroll
         for (int i = 0; i < KR; ++i) st.b[0][i] = Ld<LB, kNT>::run(rb0, vb, (uint32_t)i * rowb);
 #pragma unroll
         for (int i = 0; i < KR; ++i) st.b[1][i] = Ld<LB, kNT>::run(rb1, vb, (uint32_t)i * rowb);
-        // K past the end: the weights read as zero; zero A too so that no
+        // K past the range: the weights read as zero; zero A too so that no
         // non-finite value of a neighbouring row can leak in as 0 * inf.
         const int ka = k0 + achunk;
-        const uint32_t am = ka < Kd ? 0xffffffffu : 0u;
-        const uint4 v = Ld<16>::run(ra, va0 + (uint32_t)ka * ES, 0u);
-        st.a = make_uint4(v.x & am, v.y & am, v.z & am, v.w & am);
+        const uint32_t am = ka < ke ? 0xffffffffu : 0u;
+        st.a = mask4(Ld<16>::run(ra, va0 + (uint32_t)ka * ES, 0u), am);
     };
     auto compute = [&](const Stage &st, int step) {
-        uint4 *slot = a_lds + (step & 1) * (kATileBytes / 16);
+        uint4 *slot = a_lds + (step & 1) * kATileU4;
         slot[tid] = st.a;
         __syncthreads();
         uint4 af[NMT];
@@ -347,102 +513,307 @@ __device__ __forceinline__ void wave_gemm(const T *__restrict__ A, int a_rows,
     };
 
     constexpr int S = stages_for(NMT);
-    const int nsteps = (Kd + KSTEP - 1) / KSTEP;
+    const int nsteps = (ke - kb + KSTEP - 1) / KSTEP;
     Stage st[S];
 #pragma unroll
-    for (int j = 0; j < S - 1; ++j) load(st[j], j * KSTEP);
+    for (int j = 0; j < S - 1; ++j) load(st[j], kb + j * KSTEP);
     for (int s = 0; s < nsteps; s += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
-            // steps past the end load zero weights (no memory traffic) and add 0
-            load(st[(j + S - 1) % S], (s + j + S - 1) * KSTEP);
+            // steps past the range load zero weights (no memory traffic) and add 0
+            load(st[(j + S - 1) % S], kb + (s + j + S - 1) * KSTEP);
             __builtin_amdgcn_sched_barrier(0);
             compute(st[j], s + j);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    store_cells<T, GATEUP, NMT>(p, it, col, kg, acc, rinfo, split);
+}
 
-    // Epilogue: acc[m][mt][c][r] is the output at row 16*mt + 4*kg + r of the
-    // item and column col + c.
-    if (col >= N) return;
+// Tall cells: a run of R (2 or 4) consecutive items of one expert. The 4
+// wavefronts take row block rb = wave % R (item i0 + rb, 64 rows) and column
+// slice cs = wave / R of the C = 4/R slices of the workgroup, so the C
+// slices' weight tile is loaded once per K-step and shared through LDS by R
+// wavefronts each:
+//  * producers: the 256 threads split the tile into units of (slice, matrix,
+//    MFMA lane); a thread loads RP = KR*C/2 K-rows x 4 columns of its unit,
+//    transposes them in registers (16-bit) and writes the MFMA B fragments of
+//    that lane to LDS;
+//  * consumers: every wavefront reads its slice's fragments from LDS and its
+//    own rows' A fragments straight from memory (16-byte loads per lane).
+// Every wavefront computes 4 m-tiles (a short last item computes zero rows).
+// The weight loads keep the default cache policy here: the other runs of the
+// same expert read the same tile, often while it is still in L2.
+template <typename T, bool GATEUP, bool GATHERED, int R>
+__device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__restrict__ items,
+                                           int i0, int nitems, int g, int j, int kb, int ke,
+                                           int split, uint4 *__restrict__ lds,
+                                           float2 *__restrict__ rinfo)
+{
+    constexpr int NPL = kNpl;
+    constexpr int ES = sizeof(T);
+    constexpr int KR = Elt<T>::KR;
+    constexpr int KSTEP = 4 * KR;
+    constexpr int NMAT = 2;
+    constexpr int NMT = kMT;
+    constexpr int C = 4 / R;    // column slices per workgroup
+    constexpr int H = 2 / C;    // producer threads per (slice, matrix, lane) unit
+    constexpr int RP = KR / H;  // weight rows per producer thread
+    constexpr int SW = GATEUP ? 16 * NPL : 32 * NPL;
+    constexpr int HALF = GATEUP ? 0 : 16 * NPL;
+    constexpr int LB = NPL * ES;
+    constexpr int BUF = tall_buf_u4(C);
+    typedef typename Ld<LB>::type RowT;
+    static_assert(H * C == 2 && RP * H == KR, "tall cell shape");
+    const T *A = static_cast<const T *>(p.A);
+    const T *B0 = static_cast<const T *>(p.B0);
+    const T *B1 = static_cast<const T *>(p.B1);
+    const int Kd = p.Kd, N = p.N;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nq = lane & 15, kg = lane >> 4;
+
+    // consumer role: item i0 + rb of the run, column slice cs
+    const int rb = wave % R, cs = wave / R;
+    const WorkItem first = items[i0];
+    const int expert = first.expert;
+    WorkItem it = first;
+    if (rb != 0) {
+        if (i0 + rb < nitems) it = items[i0 + rb];
+        if (i0 + rb >= nitems || it.expert != expert) it.nrows = 0;
+    }
+    const int col = (4 * g + C * j + cs) * SW + NPL * nq;
+
+    // producer role: unit (slice pcs, matrix pm, lane plu), rows RP*hh.. of it
+    const int pcs = C == 1 ? 0 : (wave >> 1);
+    const int pm = C == 1 ? (wave >> 1) : (wave & 1);
+    const int plu = C == 1 ? ((tid >> 1) & 63) : lane;
+    const int hh = C == 1 ? (tid & 1) : 0;
+    const int pslice = 4 * g + C * j + pcs;
+    const size_t wofs = (size_t)expert * Kd * N + (size_t)kb * N;
+    const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
+    // pm and pslice are wave-uniform: keep the range and base in SGPRs
+    const uint32_t pbytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(pslice * SW >= N ? 0u : (GATEUP || pm == 0) ? kbytes : kbytes - (uint32_t)(HALF * ES)));
+    const T *pbase = GATEUP ? (pm ? B1 + wofs : B0 + wofs) : B0 + wofs + pm * HALF;
+    const __amdgpu_buffer_rsrc_t rbp = make_rsrc(pbase, pbytes);
+    const uint32_t rowb = (uint32_t)N * ES;
+    const uint32_t vpb = (uint32_t)(pslice * SW + NPL * (plu & 15)) * ES +
+                         (uint32_t)(KR * (plu >> 4) + RP * hh) * rowb;
+
+    // A: 4 m-tiles of this wavefront's item; lane row 16*mt + nq, K chunk kg
+    __amdgpu_buffer_rsrc_t ra;
+    uint32_t va[NMT];
+    if constexpr (GATHERED) {
+        ra = make_rsrc(A, (uint32_t)((size_t)p.a_rows * Kd * ES));
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
+            const int rl = 16 * mt + nq;
+            const int t = rl < it.nrows ? p.stok[it.row0 + rl] : -1;
+            va[mt] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
+        }
+    } else {
+        ra = make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rl = 16 * mt + 4 * kg + r;
-            if (rl >= it.nrows) continue;
-            const int64_t row = it.row0 + rl;
-            if constexpr (GATEUP) {
-                float hv[NPL];
+        for (int mt = 0; mt < NMT; ++mt) va[mt] = (uint32_t)(16 * mt + nq) * (uint32_t)Kd * ES;
+    }
+
+    float2 *my_rinfo = rinfo + wave * kItemRows;
+    if constexpr (!GATEUP) load_rinfo(p, it, lane, my_rinfo);
+
+    float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
-                for (int c = 0; c < NPL; ++c) hv[c] = silu(acc[0][mt][c][r]) * acc[1][mt][c][r];
-                T *H = static_cast<T *>(out) + row * N + col;
-                if constexpr (ES == 2) {
-                    static_assert(NPL == 4, "16-bit gate/up stores 4 columns per lane");
-                    store_nt(reinterpret_cast<uint2 *>(H),
-                             make_uint2(Elt<T>::pack2(hv[0], hv[1]), Elt<T>::pack2(hv[2], hv[3])));
-                } else {
-                    static_assert(NPL == 4, "fp32 gate/up stores 4 columns per lane");
-                    store_nt(reinterpret_cast<float4 *>(H), make_float4(hv[0], hv[1], hv[2], hv[3]));
-                }
-            } else {
-                static_assert(NPL == 4, "down stores 4 + 4 columns per lane");
-                const float2 ri = rinfo[rl];
-                if (__float_as_int(ri.y) < 0) continue;  // pad rows are never combined
-                const float g = ri.x;
-                float *Y = static_cast<float *>(out) + row * N + col;
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-                    if (col + m * HALF < N)
-                        store_nt(reinterpret_cast<float4 *>(Y + m * HALF),
-                                 make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
-                                             g * acc[m][mt][2][r], g * acc[m][mt][3][r]));
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int c = 0; c < NPL; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Stage {
+        RowT b[RP];
+        uint4 a[NMT];
+    };
+    auto load = [&](Stage &st, int k0) {
+        const uint32_t vb = vpb + (uint32_t)(k0 - kb) * rowb;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) st.b[i] = Ld<LB>::run(rbp, vb, (uint32_t)i * rowb);
+        const int ka = k0 + KR * kg;
+        const uint32_t am = ka < ke ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+            st.a[mt] = mask4(Ld<16>::run(ra, va[mt] + (uint32_t)ka * ES, 0u), am);
+    };
+    // fragment (or fp32 row) q of lane l of slice s, matrix m in a buffer
+    auto frag = [&](int s, int m, int q, int l) { return ((s * NMAT + m) * 4 + q) * 64 + l; };
+    auto compute = [&](const Stage &st, int step) {
+        uint4 *buf = lds + (step & 1) * BUF;
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t o[RP / 2];
+                column_of_rows<RP>(st.b, c, o);
+                if constexpr (RP == 8)
+                    buf[frag(pcs, pm, c, plu)] = make_uint4(o[0], o[1], o[2], o[3]);
+                else
+                    reinterpret_cast<uint2 *>(buf)[2 * frag(pcs, pm, c, plu) + hh] =
+                        make_uint2(o[0], o[1]);
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RP; ++i) buf[frag(pcs, pm, RP * hh + i, plu)] = st.b[i];
+        }
+        __syncthreads();
+        if constexpr (ES == 2) {
+#pragma unroll
+            for (int c = 0; c < NPL; ++c)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const uint4 fb = buf[frag(cs, m, c, lane)];
+#pragma unroll
+                    for (int mt = 0; mt < NMT; ++mt)
+                        acc[m][mt][c] = Elt<T>::mfma(st.a[mt], fb, acc[m][mt][c]);
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < KR; ++q)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const uint4 bq = buf[frag(cs, m, q, lane)];
+#pragma unroll
+                    for (int c = 0; c < NPL; ++c)
+#pragma unroll
+                        for (int mt = 0; mt < NMT; ++mt)
+                            acc[m][mt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                lanef(st.a[mt], q), lanef(bq, c), acc[m][mt][c], 0, 0, 0);
+                }
+        }
+    };
+
+    // register ring depth: 16-bit 4 (one slice) or 3 (two slices) stages;
+    // fp32 stages are larger, 2
+    constexpr int S = ES == 2 ? (C == 1 ? 4 : 3) : 2;
+    const int nsteps = (ke - kb + KSTEP - 1) / KSTEP;
+    Stage st[S];
+#pragma unroll
+    for (int jj = 0; jj < S - 1; ++jj) load(st[jj], kb + jj * KSTEP);
+    for (int s = 0; s < nsteps; s += S) {
+#pragma unroll
+        for (int jj = 0; jj < S; ++jj) {
+            load(st[(jj + S - 1) % S], kb + (s + jj + S - 1) * KSTEP);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st[jj], s + jj);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    store_cells<T, GATEUP, NMT>(p, it, col, kg, acc, my_rinfo, split);
 }
 
-// One workgroup per (work item, group of 4 column slices of 16*NPL).
-// Kd = reduction length (d for gate/up, f for down); N = output columns (f for
-// gate/up, d for down). GATEUP: B0 = W_gate, B1 = W_up, out = H (type T).
-// Otherwise: B0 = W_down, out = Y (fp32), stok/sw used in the epilogue.
-template <typename T, bool GATEUP, bool GATHERED, int NPL>
-__global__ __launch_bounds__(256, 2) void k_expert_gemm(
-    const T *__restrict__ A, int a_rows, const T *__restrict__ B0, const T *__restrict__ B1,
-    int Kd, int N,
-    const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items,
-    const int32_t *__restrict__ stok, const float *__restrict__ sw, void *__restrict__ out)
+// One workgroup per (work item, group of 4 column slices, K split).
+template <typename T, bool GATEUP, bool GATHERED>
+__global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
+                                                        const int32_t *__restrict__ ctl,
+                                                        const WorkItem *__restrict__ items)
 {
-    __shared__ uint4 a_lds[2 * kATileBytes / 16];
-    __shared__ float2 rinfo[kItemRows];
-    constexpr int SW = GATEUP ? 16 * NPL : 32 * NPL;      // columns per slice
-    const int ngroups = (N + 4 * SW - 1) / (4 * SW);      // slice groups per item
-    const int lb = xcd_logical_block(ctl[0] * ngroups);
+    __shared__ uint4 lds[kLdsU4];
+    __shared__ float2 rinfo[kWavesPerBlock * kItemRows];
+    constexpr int SW = GATEUP ? 16 * kNpl : 32 * kNpl;  // columns per slice
+    constexpr int KSTEP = 4 * Elt<T>::KR;
+    const int gs = (p.N + 4 * SW - 1) / (4 * SW);       // column groups per item
+    const int per_item = gs * p.nsplit;
+    const int nitems = ctl[0];
+    const int lb = xcd_logical_block(nitems * per_item);
     if (lb < 0) return;  // whole workgroup: no barrier reached
-    const WorkItem it = items[lb / ngroups];
+    const int i = lb / per_item;
+    const int rem = lb - i * per_item;
+    const int g = rem / p.nsplit, split = rem - g * p.nsplit;
+    const int kb = split * p.split_steps * KSTEP;
+    const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
+    const WorkItem it = items[i];
+    const int run = it.run & 0xff, j = (it.run >> 8) & 0xff;
+    if (run == 4 && j < 4 && i >= j) {
+        tall_cells<T, GATEUP, GATHERED, 4>(p, items, i - j, nitems, g, j, kb, ke, split, lds,
+                                           rinfo);
+        return;
+    }
+    if (run == 2 && j < 2 && i >= j) {
+        tall_cells<T, GATEUP, GATHERED, 2>(p, items, i - j, nitems, g, j, kb, ke, split, lds,
+                                           rinfo);
+        return;
+    }
     // wave-uniform by construction, so the buffer descriptors live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slice = (lb % ngroups) * kWavesPerBlock + wave;
+    const int slice = g * kWavesPerBlock + wave;
     switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wave_gemm<T, GATEUP, GATHERED, NPL, 1>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    case 2: wave_gemm<T, GATEUP, GATHERED, NPL, 2>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    case 3: wave_gemm<T, GATEUP, GATHERED, NPL, 3>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
-    default: wave_gemm<T, GATEUP, GATHERED, NPL, kMT>(A, a_rows, B0, B1, Kd, N, it, slice, stok, sw, out, a_lds, rinfo); break;
+    case 1: wide_cells<T, GATEUP, GATHERED, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 2: wide_cells<T, GATEUP, GATHERED, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 3: wide_cells<T, GATEUP, GATHERED, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    default: wide_cells<T, GATEUP, GATHERED, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
     }
 }
 
-// columns per lane and B stream: 4 (gate/up: 64 columns of both matrices per
-// wave; down: 2 x 64 columns of W_down per wave)
-template <typename T> constexpr int npl_down() { return 4; }
-constexpr int kNplGateUp = 4;
-
-static unsigned gemm_blocks(int64_t max_items, int N, int slice_cols)
+// ---- split-K reductions (fixed split order) --------------------------------
+__device__ __forceinline__ int rows_of_plan(const int32_t *meta, int64_t max_rows)
 {
-    int64_t blocks = max_items * ((N + 4 * slice_cols - 1) / (4 * slice_cols));
-    blocks = (blocks + 7) / 8 * 8;  // whole rounds over the 8 XCDs
-    return (unsigned)blocks;
+    const int64_t nr = meta[kMetaNr];
+    return (int)(nr < 0 ? 0 : (nr > max_rows ? max_rows : nr));
 }
 
+// h[r][c..c+3] = D(silu(sum_s G_s) * sum_s U_s) for rows r < nr
+template <typename T>
+__global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__ part,
+                                                       int64_t plane, int nsplit, int N,
+                                                       const int32_t *__restrict__ meta,
+                                                       int64_t max_rows, T *__restrict__ h)
+{
+    const int per = N / 4;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = q / per;
+    const int c = (int)(q - row * per) * 4;
+    if (row >= rows_of_plan(meta, max_rows)) return;
+    const float *P = part + row * 2 * N + c;
+    float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+    for (int s = 0; s < nsplit; ++s) {
+        const float4 gv = *reinterpret_cast<const float4 *>(P + s * plane);
+        const float4 uv = *reinterpret_cast<const float4 *>(P + s * plane + N);
+        gs = make_float4(gs.x + gv.x, gs.y + gv.y, gs.z + gv.z, gs.w + gv.w);
+        us = make_float4(us.x + uv.x, us.y + uv.y, us.z + uv.z, us.w + uv.w);
+    }
+    const float h0 = silu(gs.x) * us.x, h1 = silu(gs.y) * us.y;
+    const float h2 = silu(gs.z) * us.z, h3 = silu(gs.w) * us.w;
+    T *H = h + row * N + c;
+    if constexpr (sizeof(T) == 2)
+        store_nt(reinterpret_cast<uint2 *>(H),
+                 make_uint2(Elt<T>::pack2(h0, h1), Elt<T>::pack2(h2, h3)));
+    else
+        store_nt(reinterpret_cast<float4 *>(H), make_float4(h0, h1, h2, h3));
+}
+
+// y[r][c..c+3] = sw[r] * sum_s Y_s for rows r < nr with stok[r] >= 0
+__global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ part, int64_t plane,
+                                                     int nsplit, int N,
+                                                     const int32_t *__restrict__ stok,
+                                                     const float *__restrict__ sw,
+                                                     const int32_t *__restrict__ meta,
+                                                     int64_t max_rows, float *__restrict__ y)
+{
+    const int per = N / 4;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = q / per;
+    const int c = (int)(q - row * per) * 4;
+    if (row >= rows_of_plan(meta, max_rows) || stok[row] < 0) return;
+    const float *P = part + row * N + c;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nsplit; ++s) {
+        const float4 v = *reinterpret_cast<const float4 *>(P + s * plane);
+        a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
+    }
+    const float g = sw[row];
+    store_nt(reinterpret_cast<float4 *>(y + row * N + c),
+             make_float4(g * a.x, g * a.y, g * a.z, g * a.w));
+}
+
+// ---- host launchers --------------------------------------------------------
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, hipStream_t s)
 {
@@ -453,65 +824,102 @@ hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *s
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t gateup_t(const void *a, int a_rows, const int32_t *stok, const void *wg,
-                           const void *wu, int d, int f, const void *scratch, int64_t max_items,
-                           void *h, hipStream_t s)
+namespace {
+
+const int32_t *ctl_of(const void *scratch) { return static_cast<const int32_t *>(scratch); }
+const WorkItem *items_of(const void *scratch)
 {
-    const int32_t *ctl = static_cast<const int32_t *>(scratch);
-    const WorkItem *items =
-        reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    const dim3 grid(gemm_blocks(max_items, f, 16 * kNplGateUp));
+    return reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
+}
+
+GemmArgs gemm_args(const FfnShape &z, const void *scratch, bool gateup)
+{
+    GemmArgs p{};
+    p.part = reinterpret_cast<float *>(static_cast<char *>(const_cast<void *>(scratch)) +
+                                       z.part_offset);
+    p.nsplit = gateup ? z.split_gu : z.split_dn;
+    p.split_steps = gateup ? z.steps_gu : z.steps_dn;
+    p.plane = gateup ? z.plane_gu : z.plane_dn;
+    return p;
+}
+
+unsigned reduce_blocks(int64_t rows, int N) { return (unsigned)((rows * (N / 4) + 255) / 256); }
+
+template <typename T>
+hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, const int32_t *stok,
+                    const void *wg, const void *wu, int d, int f, const int32_t *meta,
+                    const void *scratch, void *h, hipStream_t s)
+{
+    GemmArgs p = gemm_args(z, scratch, true);
+    p.A = a;
+    p.a_rows = a_rows;
+    p.B0 = wg;
+    p.B1 = wu;
+    p.stok = stok;
+    p.out = h;
+    p.Kd = d;
+    p.N = f;
+    const dim3 grid((unsigned)z.blocks_gu);
     if (stok)  // rows gathered from x through stok
-        hipLaunchKernelGGL((k_expert_gemm<T, true, true, kNplGateUp>), grid, dim3(256), 0, s,
-                           static_cast<const T *>(a), a_rows, static_cast<const T *>(wg),
-                           static_cast<const T *>(wu), d, f, ctl, items, stok, nullptr, h);
+        hipLaunchKernelGGL((k_expert_gemm<T, true, true>), grid, dim3(256), 0, s, p,
+                           ctl_of(scratch), items_of(scratch));
     else
-        hipLaunchKernelGGL((k_expert_gemm<T, true, false, kNplGateUp>), grid, dim3(256), 0, s,
-                           static_cast<const T *>(a), 0, static_cast<const T *>(wg),
-                           static_cast<const T *>(wu), d, f, ctl, items, nullptr, nullptr, h);
+        hipLaunchKernelGGL((k_expert_gemm<T, true, false>), grid, dim3(256), 0, s, p,
+                           ctl_of(scratch), items_of(scratch));
+    if (z.split_gu > 1)
+        hipLaunchKernelGGL(k_reduce_gateup<T>, dim3(reduce_blocks(z.max_rows, f)), dim3(256), 0, s,
+                           p.part, p.plane, p.nsplit, f, meta, z.max_rows, static_cast<T *>(h));
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t down_t(const void *h, const void *wd, int d, int f, const int32_t *stok,
-                         const float *sw, const void *scratch, int64_t max_items, float *y,
-                         hipStream_t s)
+hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f,
+                  const int32_t *stok, const float *sw, const int32_t *meta, const void *scratch,
+                  float *y, hipStream_t s)
 {
-    const int32_t *ctl = static_cast<const int32_t *>(scratch);
-    const WorkItem *items =
-        reinterpret_cast<const WorkItem *>(static_cast<const char *>(scratch) + kCtlBytes);
-    hipLaunchKernelGGL((k_expert_gemm<T, false, false, npl_down<T>()>),
-                       dim3(gemm_blocks(max_items, d, 32 * npl_down<T>())), dim3(256), 0, s,
-                       static_cast<const T *>(h), 0, static_cast<const T *>(wd), nullptr, f, d, ctl,
-                       items, stok, sw, static_cast<void *>(y));
+    GemmArgs p = gemm_args(z, scratch, false);
+    p.A = h;
+    p.B0 = wd;
+    p.stok = stok;
+    p.sw = sw;
+    p.out = y;
+    p.Kd = f;
+    p.N = d;
+    hipLaunchKernelGGL((k_expert_gemm<T, false, false>), dim3((unsigned)z.blocks_dn), dim3(256),
+                       0, s, p, ctl_of(scratch), items_of(scratch));
+    if (z.split_dn > 1)
+        hipLaunchKernelGGL(k_reduce_down, dim3(reduce_blocks(z.max_rows, d)), dim3(256), 0, s,
+                           p.part, p.plane, p.nsplit, d, stok, sw, meta, z.max_rows, y);
     return hipGetLastError();
 }
 
-hipError_t launch_gateup(int dtype, const void *xs, const void *wg, const void *wu, int d, int f,
-                         const void *scratch, int64_t max_items, void *h, hipStream_t s)
+}  // namespace
+
+hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const void *wg,
+                         const void *wu, int d, int f, const int32_t *meta, const void *scratch,
+                         void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
-    return gateup_t<float>(xs, 0, nullptr, wg, wu, d, f, scratch, max_items, h, s);
+    if (dtype == 1) return gateup_t<_Float16>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2) return gateup_t<__bf16>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_t<float>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
 }
 
-hipError_t launch_gateup_gathered(int dtype, const void *x, int T, const int32_t *stok,
-                                  const void *wg, const void *wu, int d, int f, const void *scratch,
-                                  int64_t max_items, void *h, hipStream_t s)
+hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,
+                                  const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
-    return gateup_t<float>(x, T, stok, wg, wu, d, f, scratch, max_items, h, s);
+    if (dtype == 1) return gateup_t<_Float16>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2) return gateup_t<__bf16>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_t<float>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
 }
 
-hipError_t launch_down(int dtype, const void *h, const void *wd, int d, int f, const int32_t *stok,
-                       const float *sw, const void *scratch, int64_t max_items, float *y,
-                       hipStream_t s)
+hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *wd, int d, int f,
+                       const int32_t *stok, const float *sw, const int32_t *meta,
+                       const void *scratch, float *y, hipStream_t s)
 {
-    if (dtype == 1) return down_t<_Float16>(h, wd, d, f, stok, sw, scratch, max_items, y, s);
-    if (dtype == 2) return down_t<__bf16>(h, wd, d, f, stok, sw, scratch, max_items, y, s);
-    return down_t<float>(h, wd, d, f, stok, sw, scratch, max_items, y, s);
+    if (dtype == 1) return down_t<_Float16>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+    if (dtype == 2) return down_t<__bf16>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+    return down_t<float>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
 }
 
 }  // namespace moe

@@ -40,18 +40,33 @@ hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, 
 int ffn_rows_per_item();
 // bound on the number of work items for a plan of max_rows rows
 int64_t ffn_max_items(int E, int tm, int64_t max_rows);
-size_t ffn_scratch_bytes(int E, int tm, int64_t max_rows);
+
+// Launch shape of the two grouped GEMMs for a plan bound (host side): K
+// splits, grid sizes and the layout of the FFN scratch (item count, work
+// items, then the split-K partial planes when a GEMM is split).
+struct FfnShape {
+    int64_t max_items, max_rows;
+    int split_gu, steps_gu;  // gate/up: K splits and K-steps per split
+    int split_dn, steps_dn;  // down
+    int64_t blocks_gu, blocks_dn;  // workgroups per launch
+    int64_t plane_gu, plane_dn;    // floats per partial plane
+    size_t part_offset;            // byte offset of the partial planes
+    size_t scratch_bytes;
+};
+FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype);
+
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, hipStream_t s);
-hipError_t launch_gateup(int dtype, const void *xs, const void *wg, const void *wu, int d, int f,
-                         const void *scratch, int64_t max_items, void *h, hipStream_t s);
+hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const void *wg,
+                         const void *wu, int d, int f, const int32_t *meta, const void *scratch,
+                         void *h, hipStream_t s);
 // gate/up reading row r straight from x[stok[r]] (the gather fused into the
 // A-tile loads); x must be smaller than 2 GiB.
-hipError_t launch_gateup_gathered(int dtype, const void *x, int T, const int32_t *stok,
-                                  const void *wg, const void *wu, int d, int f, const void *scratch,
-                                  int64_t max_items, void *h, hipStream_t s);
-hipError_t launch_down(int dtype, const void *h, const void *wd, int d, int f, const int32_t *stok,
-                       const float *sw, const void *scratch, int64_t max_items, float *y,
-                       hipStream_t s);
+hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,
+                                  const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s);
+hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *wd, int d, int f,
+                       const int32_t *stok, const float *sw, const int32_t *meta,
+                       const void *scratch, float *y, hipStream_t s);
 
 }  // namespace moe

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
                         it.expert = tid;
                         it.row0 = r0;
                         it.nrows = min(min(kItemRows, rows - q * kItemRows), max_rows - r0);
-                        it.pad = 0;
+                        it.run = item_run(q, nit);
                         items[idx] = it;
                     }
                 }

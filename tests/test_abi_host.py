@@ -80,7 +80,7 @@ def test_gather_combine_ffn_forward_reject_bad_arguments():
     assert L.moe_combine(A, 64, A, 0, 2, 16, A, None) == 1          # T < 1
     assert L.moe_combine(A + 4, 64, A, 4, 2, 16, A, None) == 1      # y misaligned
     need = ctypes.c_size_t()
-    assert L.moe_ffn_scratch_bytes(8, 16, 256, ctypes.byref(need)) == 0
+    assert L.moe_ffn_scratch_bytes(8, 64, 128, 16, 256, 1, ctypes.byref(need)) == 0
     args = [A, A, A, A, 1, 8, 64, 128, 16, A, A, A, A, 256, A, A, A]
     assert L.moe_expert_ffn(*args, need.value - 1, None) == 1       # small scratch
     bad = list(args)

@@ -1,7 +1,10 @@
 """GPU parity of moe_expert_ffn alone, fed the oracle's plan and gathered rows:
 the SwiGLU output h and the weighted expert output y of every (sampled) entry
 against the oracle's per-entry loop, max|d|/max|ref| within the tolerance of
-the element type (1e-5 fp32, 5e-3 fp16/bf16). Pad rows of y stay untouched."""
+the element type (1e-5 fp32, 5e-3 fp16/bf16). Pad rows of y stay untouched.
+Shapes are chosen to take every launch path: K split into ranges (few work
+items) in either projection, and runs of 2 or 4 work items of one expert that
+share the weight tile (experts with more than 64 rows)."""
 import numpy as np
 import pytest
 import torch
@@ -29,8 +32,9 @@ def run_ffn(case, ids, w, x, entries=None):
     es = synth.ELEM_BYTES[cfg.dtype]
     h = polluted(R * cfg.f * es // 4)
     y = polluted(R * cfg.d, torch.float32)
-    scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.tm, R), dtype=torch.uint8,
-                          device="cuda")
+    scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R,
+                                                    abi.DTYPE_NAME[cfg.dtype]),
+                          dtype=torch.uint8, device="cuda")
     say(f"[ffn] {cfg.name}: T={T} d={cfg.d} E={cfg.E} K={K} f={cfg.f} {cfg.dtype} tm={cfg.tm} "
         f"nr={nr}")
     abi.moe_expert_ffn(dev(xs, cfg.dtype), case.d("wg"), case.d("wu"), case.d("wd"),
@@ -88,3 +92,43 @@ def test_ffn_configs_sampled(name):
         ent = np.unique(np.concatenate([ent, heavy[:: max(1, len(heavy) // 24)]]))
     run_ffn(case, ids, w, x, ent.astype(np.int32))
     case.drop_device()
+
+
+def item_runs(cfg, ids):
+    """run lengths (1, 2, 4) of the work items the plan of `ids` yields: items of
+    64 rows per expert, grouped 4 by 4, then a pair, then singles"""
+    cnt = np.bincount(ids[(ids >= 0) & (ids < cfg.E)].ravel(), minlength=cfg.E)
+    rows = (cnt + cfg.tm - 1) // cfg.tm * cfg.tm
+    runs = {1: 0, 2: 0, 4: 0}
+    for n in (rows + 63) // 64:
+        runs[4] += n // 4
+        rest = n % 4
+        runs[2] += 1 if rest >= 2 else 0
+        runs[1] += rest % 2
+    return runs
+
+
+# (config, expect gate/up split, expect down split, expect runs of 4 or 2)
+PATHS = [
+    (custom("split_gateup_f32", T=8, d=1024, E=16, K=2, f=128, dtype="f32"), True, False, False),
+    (custom("split_both_bf16", T=6, d=1536, E=64, K=4, f=1024, dtype="bf16"), True, True, False),
+    (custom("tall4_split_f16", T=600, d=2048, E=2, K=1, f=256, dtype="f16"), True, False, True),
+    (custom("tall4_split_bf16_tm1", T=700, d=1024, E=3, K=1, f=512, dtype="bf16", tm=1), True,
+     True, True),
+    (custom("tall_mix_f32", T=400, d=256, E=4, K=2, f=192, dtype="f32", bias="zipf1.1"), True,
+     False, True),
+    (custom("tall_split_unit_f16", T=2048, d=512, E=8, K=2, f=1024, dtype="f16", bias="zipf1.1",
+            x_std=1.0), True, True, True),
+]
+
+
+@pytest.mark.parametrize("cfg,sgu,sdn,tall", PATHS, ids=[c[0].name for c in PATHS])
+def test_ffn_launch_paths(cfg, sgu, sdn, tall):
+    case = make_case(cfg)
+    z = abi.moe_plan_sizes(cfg.T, cfg.K, cfg.E, cfg.tm)
+    splits = abi.moe_ffn_splits(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows, abi.DTYPE_NAME[cfg.dtype])
+    assert (splits[0] > 1, splits[1] > 1) == (sgu, sdn), splits
+    runs = item_runs(cfg, case.ids)
+    assert (runs[4] + runs[2] > 0) == tall, runs
+    say(f"[ffn paths] {cfg.name}: splits={splits} runs={runs}")
+    run_ffn(case, case.ids, case.w, case.x)

@@ -43,7 +43,18 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+# shapes that split K (few work items) and that run several work items of one
+# expert against a shared weight tile, with the gather fused into the loads
+PATHS = [
+    custom("split_both_bf16", T=6, d=1536, E=64, K=4, f=1024, dtype="bf16"),
+    custom("tall4_split_f16", T=600, d=2048, E=2, K=1, f=256, dtype="f16"),
+    custom("tall_mix_f32", T=400, d=256, E=4, K=2, f=192, dtype="f32", bias="zipf1.1"),
+    custom("tall_split_unit_bf16", T=2048, d=512, E=8, K=2, f=1024, dtype="bf16",
+           bias="zipf1.1", x_std=1.0),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL + PATHS, ids=[c.name for c in SMALL + PATHS])
 def test_forward_small_all_tokens(cfg):
     case = make_case(cfg)
     say(f"[forward] {cfg.name}")
@@ -85,9 +96,13 @@ def test_forward_long_prompt_all_chunks():
     case.drop_device()
 
 
-def test_forward_deterministic():
-    cfg = synth.CONFIGS["prefill_fp16"]
+@pytest.mark.parametrize("cfg", [synth.CONFIGS["prefill_fp16"], synth.CONFIGS["decode_bf16"],
+                                 PATHS[-1]], ids=["prefill_fp16", "decode_bf16_split",
+                                                  "tall_split_unit_bf16"])
+def test_forward_deterministic(cfg):
+    """bitwise equal on a second call (split-K partials are added in a fixed order)"""
     case = make_case(cfg)
+    say(f"[forward determinism] {cfg.name}")
     a, ws = gpu_forward(case, case.ids, case.w, case.x)
     b, _ = gpu_forward(case, case.ids, case.w, case.x, ws)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
