@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_RECORD = os.path.join(PROFILES, "prefill_fp16_hbm_traffic.md")
+TIMER_EVERY = 5  # timed steps that also record the gate/up kernel's HIP events
 GEMM_SOURCES = ["mixture_experts_routed_amd/csrc/ffn.hip", "mixture_experts_routed_amd/csrc/common.hpp"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -257,8 +258,9 @@ def main():
     ws = torch.empty(abi.moe_forward_workspace(T, K, E, d, f, tm, abi.DTYPE_NAME[cfg.dtype]),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
-    # timed steps record events around the gate/up kernel only; every stage is
-    # timed in a separate pass afterwards (its events add launch gaps)
+    # timed steps record events around the gate/up kernel only, on every
+    # TIMER_EVERY-th step (each event pair adds a few us of launch gap); every
+    # stage is timed in a separate pass afterwards
     timer = abi.Timer(capacity=max(args.steps * ncalls, 1), stages=("gateup",))
 
     def step(tmr=None):
@@ -280,8 +282,8 @@ def main():
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(timer)
+    for i in range(args.steps):
+        step(timer if i % TIMER_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
@@ -293,6 +295,43 @@ def main():
     torch.cuda.synchronize()
     st_all = breakdown.read()
     breakdown.close()
+
+    # per-step distribution (one event pair around each step, after the timed
+    # steps): warm = back to back; cold = a 1 GiB buffer written before each step
+    # evicts the 256 MB Infinity Cache and the L2s first
+    ndist = max(1, min(args.steps, 30))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def distribution(cold: bool) -> dict:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(ndist)]
+        for a, b in evs:
+            if cold:
+                flush.fill_(1)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        return {q: round(float(np.percentile(v, p)), 1) for q, p in (("p10", 10), ("p50", 50),
+                                                                     ("p90", 90))}
+
+    step_us = {"warm": distribution(False), "cold": distribution(True), "samples": ndist}
+
+    # a plain device copy of 1 GiB (torch's copy kernel, read + write), for the
+    # streaming rate this machine reaches outside the library
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = flush.view(torch.float32)
+    for _ in range(2):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del flush, src, dst
 
     # the router step before the layer (moe_route_topk on the first call's logits),
     # timed on its own: it is not part of the layer step above
@@ -331,13 +370,20 @@ def main():
         "route_us": route_us,
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},
         "stages_note": "per-kernel HIP events in a pass after the timed steps (events around "
-                       "every kernel); the timed steps record the gate/up kernel only",
+                       "every kernel); the timed steps record the gate/up kernel only, on every "
+                       f"{TIMER_EVERY}th step",
+        "step_us_note": "one event pair per step, after the timed steps; cold: a 1 GiB buffer "
+                        "is written before each step",
         "stages_gbs": {k: round(b / (us[k] * 1e3), 1) for k, b in stage_bytes(cfg, meta, T).items()
                        if us.get(k)},
+        "step_us": step_us,
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
         "roofline": {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": recorded_traffic("k_expert_gemm/gateup"),
+                     "copy_gbs": round(copy_gbs, 1),
+                     "copy_note": "same run: torch's device copy of 1 GiB of fp32 (bytes read "
+                                  "+ written) reaches this rate",
                      "algorithmic_bytes_per_launch": gu_bytes},
     }
     if args.workload != "prefill_fp16":

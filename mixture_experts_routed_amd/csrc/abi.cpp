@@ -185,7 +185,7 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
         const hipError_t e =
             x ? moe::launch_gateup_gathered(z, dtype, x, T, stok, wg, wu, d, f, meta, scratch, h,
                                             s)
-              : moe::launch_gateup(z, dtype, xs, wg, wu, d, f, meta, scratch, h, s);
+              : moe::launch_gateup(z, dtype, xs, stok, wg, wu, d, f, meta, scratch, h, s);
         if (e != hipSuccess) return MOE_EHIP;
     }
     {

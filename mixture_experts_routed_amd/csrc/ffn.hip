@@ -313,6 +313,8 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
             const int64_t row = it.row0 + rl;
             if constexpr (GATEUP) {
                 if (partial) {
+                    // pad rows: the reduction writes their zero h without reading
+                    if (__float_as_int(rinfo[rl].y) < 0) continue;
                     float *P = p.part + split * p.plane + row * 2 * N + col;
 #pragma unroll
                     for (int m = 0; m < 2; ++m)
@@ -351,13 +353,15 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
     }
 }
 
-// (router weight, token) of the item's rows for the down epilogue
+// (router weight, token) of the item's rows for the epilogue; the gate/up
+// projection has no router weight (sw is not passed) and needs the tokens only
+template <bool WITH_SW>
 __device__ __forceinline__ void load_rinfo(const GemmArgs &p, const WorkItem &it, int l,
                                            float2 *__restrict__ rinfo)
 {
     const bool ok = l < it.nrows;
     const int64_t r = it.row0 + (ok ? l : 0);
-    rinfo[l] = make_float2(ok ? p.sw[r] : 0.f, __int_as_float(ok ? p.stok[r] : -1));
+    rinfo[l] = make_float2(WITH_SW && ok ? p.sw[r] : 0.f, __int_as_float(ok ? p.stok[r] : -1));
 }
 
 // Pipeline depth of the wide cells for NMT m-tiles: stage = 32 B-operand + 4
@@ -448,9 +452,10 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
         va0 = (uint32_t)arow * (uint32_t)Kd * ES;
     }
 
-    // made visible to all wavefronts by the barriers of the K loop
-    if constexpr (!GATEUP)
-        if (tid < kItemRows) load_rinfo(p, it, tid, rinfo);
+    // made visible to all wavefronts by the barriers of the K loop (gate/up
+    // needs the tokens only for its partial sums)
+    if (!GATEUP || p.nsplit > 1)
+        if (tid < kItemRows) load_rinfo<!GATEUP>(p, it, tid, rinfo);
 
     float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
@@ -620,7 +625,7 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
     }
 
     float2 *my_rinfo = rinfo + wave * kItemRows;
-    if constexpr (!GATEUP) load_rinfo(p, it, lane, my_rinfo);
+    if (!GATEUP || p.nsplit > 1) load_rinfo<!GATEUP>(p, it, lane, my_rinfo);
 
     float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
@@ -759,10 +764,12 @@ __device__ __forceinline__ int rows_of_plan(const int32_t *meta, int64_t max_row
     return (int)(nr < 0 ? 0 : (nr > max_rows ? max_rows : nr));
 }
 
-// h[r][c..c+3] = D(silu(sum_s G_s) * sum_s U_s) for rows r < nr
+// h[r][c..c+3] = D(silu(sum_s G_s) * sum_s U_s) for rows r < nr; pad rows
+// (stok < 0, whose partial sums are not stored) get h = 0, as unsplit
 template <typename T>
 __global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__ part,
                                                        int64_t plane, int nsplit, int N,
+                                                       const int32_t *__restrict__ stok,
                                                        const int32_t *__restrict__ meta,
                                                        int64_t max_rows, T *__restrict__ h)
 {
@@ -773,7 +780,8 @@ __global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__
     if (row >= rows_of_plan(meta, max_rows)) return;
     const float *P = part + row * 2 * N + c;
     float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
-    for (int s = 0; s < nsplit; ++s) {
+    const int ns = stok[row] < 0 ? 0 : nsplit;
+    for (int s = 0; s < ns; ++s) {
         const float4 gv = *reinterpret_cast<const float4 *>(P + s * plane);
         const float4 uv = *reinterpret_cast<const float4 *>(P + s * plane + N);
         gs = make_float4(gs.x + gv.x, gs.y + gv.y, gs.z + gv.z, gs.w + gv.w);
@@ -846,9 +854,9 @@ GemmArgs gemm_args(const FfnShape &z, const void *scratch, bool gateup)
 unsigned reduce_blocks(int64_t rows, int N) { return (unsigned)((rows * (N / 4) + 255) / 256); }
 
 template <typename T>
-hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, const int32_t *stok,
-                    const void *wg, const void *wu, int d, int f, const int32_t *meta,
-                    const void *scratch, void *h, hipStream_t s)
+hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
+                    const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                    const int32_t *meta, const void *scratch, void *h, hipStream_t s)
 {
     GemmArgs p = gemm_args(z, scratch, true);
     p.A = a;
@@ -860,7 +868,7 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, const int32_t 
     p.Kd = d;
     p.N = f;
     const dim3 grid((unsigned)z.blocks_gu);
-    if (stok)  // rows gathered from x through stok
+    if (gathered)  // rows gathered from x through stok
         hipLaunchKernelGGL((k_expert_gemm<T, true, true>), grid, dim3(256), 0, s, p,
                            ctl_of(scratch), items_of(scratch));
     else
@@ -868,7 +876,8 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, const int32_t 
                            ctl_of(scratch), items_of(scratch));
     if (z.split_gu > 1)
         hipLaunchKernelGGL(k_reduce_gateup<T>, dim3(reduce_blocks(z.max_rows, f)), dim3(256), 0, s,
-                           p.part, p.plane, p.nsplit, f, meta, z.max_rows, static_cast<T *>(h));
+                           p.part, p.plane, p.nsplit, f, stok, meta, z.max_rows,
+                           static_cast<T *>(h));
     return hipGetLastError();
 }
 
@@ -895,22 +904,24 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
 
 }  // namespace
 
-hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const void *wg,
-                         const void *wu, int d, int f, const int32_t *meta, const void *scratch,
-                         void *h, hipStream_t s)
+hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const int32_t *stok,
+                         const void *wg, const void *wu, int d, int f, const int32_t *meta,
+                         const void *scratch, void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
-    return gateup_t<float>(z, xs, 0, nullptr, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 1)
+        return gateup_t<_Float16>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2)
+        return gateup_t<__bf16>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_t<float>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
 }
 
 hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
                                   const int32_t *meta, const void *scratch, void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
-    return gateup_t<float>(z, x, T, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 1) return gateup_t<_Float16>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2) return gateup_t<__bf16>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_t<float>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
 }
 
 hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *wd, int d, int f,

@@ -57,9 +57,9 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype);
 
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, hipStream_t s);
-hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const void *wg,
-                         const void *wu, int d, int f, const int32_t *meta, const void *scratch,
-                         void *h, hipStream_t s);
+hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const int32_t *stok,
+                         const void *wg, const void *wu, int d, int f, const int32_t *meta,
+                         const void *scratch, void *h, hipStream_t s);
 // gate/up reading row r straight from x[stok[r]] (the gather fused into the
 // A-tile loads); x must be smaller than 2 GiB.
 hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,

@@ -51,6 +51,10 @@ PATHS = [
     custom("tall_mix_f32", T=400, d=256, E=4, K=2, f=192, dtype="f32", bias="zipf1.1"),
     custom("tall_split_unit_bf16", T=2048, d=512, E=8, K=2, f=1024, dtype="bf16",
            bias="zipf1.1", x_std=1.0),
+    # T*K = 40,960 > 32,768: the plan runs as three launches and the work list
+    # is written by its own kernel
+    custom("three_launch_plan_f16", T=4096, d=128, E=48, K=10, f=64, dtype="f16",
+           bias="normal0.5"),
 ]
 
 
