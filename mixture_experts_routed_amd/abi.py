@@ -66,6 +66,7 @@ _SIGS = {
     "moe_timer_create": [ctypes.POINTER(P), I32, ctypes.c_uint],
     "moe_timer_destroy": [P],
     "moe_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+    "moe_stream_read": [P, SZ, P, I32, P],
 }
 
 EXPORTS = tuple(_SIGS) + ("moe_status_str",)
@@ -145,6 +146,13 @@ def moe_forward_layout(T, K, E, d, f, tm, dtype: int) -> ForwardLayout:
     L = ForwardLayout()
     _check("moe_forward_layout", lib().moe_forward_layout(T, K, E, d, f, tm, dtype, ctypes.byref(L)))
     return L
+
+
+def moe_stream_read(src, sink, stream=None):
+    """Measurement only: one streaming read of the GPU tensor `src` (see the header)."""
+    nbytes = src.numel() * src.element_size()
+    _check("moe_stream_read", lib().moe_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink"),
+                                                    sink.numel(), _stream(stream)))
 
 
 def moe_status_str(status: int) -> str:

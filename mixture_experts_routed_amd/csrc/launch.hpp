@@ -69,4 +69,10 @@ hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *
                        const int32_t *stok, const float *sw, const int32_t *meta,
                        const void *scratch, float *y, hipStream_t s);
 
+// ---- measurement only ----
+// one streaming read of `bytes` (16-byte words) of src; sink holds sink_words
+// words, one per workgroup (written only for one checksum value in 2^32)
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
+                              hipStream_t s);
+
 }  // namespace moe

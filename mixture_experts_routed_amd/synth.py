@@ -16,7 +16,12 @@ and routing statistics:
   sweep-prefill ..., Motivation);
 * a handful of tokens routed top-8, M of about 1 per expert (Batched resident
   MoE experts on Apple Silicon ..., Contribution);
-* a 32K prompt processed in 2048-token chunks (#372 Prompt path ..., Speed).
+* a 32K prompt processed in 2048-token chunks (#372 Prompt path ..., Speed);
+* the prefill shape with tail skipping: a token's lowest-weight top-k slots
+  routed to no expert (id -1), as in the plan's parity runs (Round 4 Track C
+  audit, section 3). The pages do not give the skipping rule; here a slot is
+  skipped when its renormalised weight is below 0.75/K (about 23% of the slots
+  at this shape; the top-1 slot is never skipped).
 
 Every random stream is numpy PCG64 seeded by SeedSequence([seed, tag, e]), so
 any single expert's weights can be regenerated on their own.
@@ -51,6 +56,7 @@ class Config:
     tm: int = 16    # row padding: each expert's row count is rounded up to tm
     chunk: int = 0  # tokens per layer call (0: all T in one call)
     bias: str = "none"  # per-expert router bias: none | normal0.5 | zipf1.1
+    tail_skip: float = 0.0  # slots with weight < tail_skip / K get id -1
     x_std: float = 0.02
     w_std: float = 0.02
     seed: int = 0
@@ -72,6 +78,8 @@ CONFIGS = {
                           bias="normal0.5", seed=1004),
     "long_skewed_fp16": Config("long_skewed_fp16", T=32768, d=2560, E=512, K=10, f=768, dtype="f16",
                                chunk=2048, bias="zipf1.1", seed=1005),
+    "prefill_tailskip_fp16": Config("prefill_tailskip_fp16", T=2048, d=2560, E=512, K=10, f=768,
+                                    dtype="f16", tail_skip=0.75, seed=1006),
 }
 CONFIG_ORDER = list(CONFIGS)
 
@@ -127,7 +135,9 @@ def routing(cfg: Config, T: int | None = None):
 
     logits = N(0,1) + bias (fp64); softmax over the E experts; the K largest
     probabilities in descending order (ties to the lower expert id) are kept
-    and renormalised to sum to one. Column k of ids is the k-th choice.
+    and renormalised to sum to one. Column k of ids is the k-th choice. With
+    tail skipping, slots whose weight is below tail_skip / K get id -1 (their
+    weight is left in w; a skipped slot contributes nothing).
     """
     T = cfg.T if T is None else T
     logits = rng(cfg.seed, TAG_LOGITS).standard_normal((T, cfg.E)) + router_bias(cfg)[None, :]
@@ -135,8 +145,11 @@ def routing(cfg: Config, T: int | None = None):
     p = np.exp(logits - logits.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
     pk = np.take_along_axis(p, order, axis=1)
-    w = pk / pk.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), w.astype(np.float32)
+    w = (pk / pk.sum(axis=1, keepdims=True)).astype(np.float32)
+    ids = order.astype(np.int32)
+    if cfg.tail_skip > 0:
+        ids[w < np.float32(cfg.tail_skip / cfg.K)] = -1
+    return ids, w
 
 
 def router_logits(cfg: Config, T: int | None = None) -> np.ndarray:

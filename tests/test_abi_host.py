@@ -97,6 +97,14 @@ def test_gather_combine_ffn_forward_reject_bad_arguments():
                          None) == 1                                   # workspace not 256-aligned
 
 
+def test_stream_read_rejects_bad_arguments():
+    L = abi.lib()
+    assert L.moe_stream_read(A + 8, 1 << 20, A, 16, None) == 1   # src not 16-byte aligned
+    assert L.moe_stream_read(A, 8, A, 16, None) == 1             # fewer than 16 bytes
+    assert L.moe_stream_read(A, 1 << 20, A, 0, None) == 1        # no sink
+    assert L.moe_stream_read(None, 1 << 20, A, 16, None) == 1
+
+
 def test_forward_layout_is_consistent():
     L = abi.moe_forward_layout(2048, 10, 512, 2560, 768, 16, abi.MOE_F16)
     z = abi.moe_plan_sizes(2048, 10, 512, 16)

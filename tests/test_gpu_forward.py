@@ -72,7 +72,8 @@ def sample_tokens(T, seed, n=24):
         np.int32)
 
 
-@pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16"])
+@pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16",
+                                  "prefill_tailskip_fp16"])
 def test_forward_full_size_sampled(name):
     cfg = synth.CONFIGS[name]
     case = make_case(cfg)
