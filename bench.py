@@ -55,6 +55,17 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def gemm_is_gateup(name: str) -> bool:
+    """k_expert_gemm<T, GATEUP, GATHERED, PACKED>: GATEUP from the (mangled or
+    demangled) kernel name"""
+    import re
+    m = re.search(r"k_expert_gemmI(?:DF16_|DF16b|f)Lb([01])E", name)
+    if m:
+        return m.group(1) == "1"
+    m = re.search(r"k_expert_gemm<[^,]+,\s*(true|false)", name)
+    return bool(m) and m.group(1) == "true"
+
+
 def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> dict:
     """Per-kernel HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch), each scaled by what the same counter reads for a plain device copy of known size
@@ -76,8 +87,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> 
     def short(name):
         m = re.search(r"moe::(k_\w+)|_ZN3moe(\d+)(k_\w+?)I", name)
         if "k_expert_gemm" in name:
-            kind = "gateup" if ("Lb1E" in name or "true" in name) else "down"
-            return f"k_expert_gemm/{kind}"
+            return f"k_expert_gemm/{'gateup' if gemm_is_gateup(name) else 'down'}"
         if m:
             return m.group(1) or m.group(3)
         return name[:40]
@@ -151,6 +161,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_fp16")
+    ap.add_argument("--weights", choices=("packed", "rowmajor"), default="packed",
+                    help="expert weights as moe_pack_weights lays them out (packed once before "
+                         "the timed steps) or row-major as generated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock target of the CPU oracle sample")
@@ -250,6 +263,14 @@ def main():
 
     dev = torch.device("cuda:0")
     wts = {k: up(synth.expert_weights(cfg, k)) for k in ("gate", "up", "down")}
+    packed, pack_ms = None, None
+    if args.weights == "packed":
+        # one-time layout change of the weights (model load), outside the steps
+        torch.cuda.synchronize()
+        tp = time.perf_counter()
+        packed = abi.pack(wts["gate"], wts["up"], wts["down"])
+        torch.cuda.synchronize()
+        pack_ms = (time.perf_counter() - tp) * 1e3
     xd, idsd, wd = up(x), torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
     chunks = [(xd[c * T:(c + 1) * T], idsd[c * T:(c + 1) * T], wd[c * T:(c + 1) * T])
               for c in range(ncalls)]
@@ -266,7 +287,7 @@ def main():
     def step(tmr=None):
         for cx, cids, cw in chunks:
             abi.forward(cx, cids, cw, wts["gate"], wts["up"], wts["down"], tm=tm, workspace=ws,
-                        out=out, timer=tmr)
+                        out=out, timer=tmr, packed=packed)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -366,7 +387,12 @@ def main():
                    "routing": {"none": "router logits N(0,1)", "normal0.5": "router logits N(0,1) "
                                "+ per-expert N(0,0.5) bias", "zipf1.1": "router logits N(0,1) + "
                                "Zipf(1.1)-ranked per-expert bias"}[cfg.bias] +
-                              ", softmax top-k renormalised"},
+                              ", softmax top-k renormalised" +
+                              (", tail-skipped slots (weight < %.2f/K) routed nowhere" % cfg.tail_skip
+                               if cfg.tail_skip else ""),
+                   "weights": ("packed once into the MFMA tile layout by moe_pack_weights before "
+                               "the timed steps (%.1f ms)" % pack_ms) if packed is not None
+                              else "row-major [E][d][f] / [E][f][d] as generated"},
         "plan_us": us["hist"] + us["scan"] + us["place"],
         "route_us": route_us,
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},

@@ -211,6 +211,54 @@ int moe_expert_ffn(const void *xs, const void *w_gate, const void *w_up, const v
                    const float *sw, const int32_t *meta, int64_t max_rows, void *h, float *y,
                    void *scratch, size_t scratch_bytes, moe_stream_t stream);
 
+/* Which matrices a packed weight buffer holds. */
+enum moe_wkind {
+    MOE_W_GATE_UP = 0, /* W_gate or W_up: [E][d][f] */
+    MOE_W_DOWN = 1     /* W_down: [E][f][d] */
+};
+
+/*
+ * moe_packed_weight_bytes -- host only: size of one packed matrix set (see
+ * moe_pack_weights) for E experts, hidden size d, intermediate size f, dtype.
+ * Errors: MOE_EINVAL for NULL bytes, E < 1, d or f not positive multiples of
+ * 8, bad dtype or kind; MOE_EUNSUPPORTED for E > MOE_MAX_EXPERTS.
+ */
+int moe_packed_weight_bytes(int E, int d, int f, int dtype, int kind, size_t *bytes);
+
+/*
+ * moe_pack_weights -- rearrange one set of expert matrices, once (at model
+ * load), into the tile layout the grouped FFN streams: for each expert,
+ * column group of 4 slices, K-step and slice, one contiguous 4 KB tile per
+ * 64-column stream (gate/up: one stream of 64 columns per slice; down: two)
+ * holding, for each of the 64 MFMA lanes, the 4 B-operand words of that step
+ * in the order the lane consumes them (16-bit types: 8 consecutive K of one
+ * column; fp32: 4 consecutive columns of one K-row). Bits are copied, nothing
+ * is converted; positions past d or f hold zeros. The grouped GEMMs then read
+ * each workgroup's K range of a column group as one contiguous run, with
+ * 16-byte loads and no transposes: a reorganisation of [P3]'s resident expert
+ * weights for the MI355X memory system, not a change of the arithmetic
+ * (moe_forward_packed returns the same bits as moe_forward).
+ * In:  w = W_gate or W_up [E][d][f] (kind MOE_W_GATE_UP) or W_down [E][f][d]
+ *      (MOE_W_DOWN) of dtype, 16-byte aligned.
+ * Out: packed [moe_packed_weight_bytes], 16-byte aligned; owned by the caller.
+ * Errors: as moe_packed_weight_bytes, plus MOE_EINVAL for misaligned pointers,
+ * packed_bytes too small, or one matrix of 2 GiB or more; MOE_EHIP on a failed
+ * launch.
+ */
+int moe_pack_weights(const void *w, int dtype, int E, int d, int f, int kind, void *packed,
+                     size_t packed_bytes, moe_stream_t stream);
+
+/*
+ * moe_expert_ffn_packed -- moe_expert_ffn with packed expert weights
+ * (pw_gate, pw_up: moe_pack_weights(..., MOE_W_GATE_UP); pw_down:
+ * MOE_W_DOWN). Same arguments, results (bit for bit) and errors otherwise.
+ */
+int moe_expert_ffn_packed(const void *xs, const void *pw_gate, const void *pw_up,
+                          const void *pw_down, int dtype, int E, int d, int f, int tm,
+                          const int32_t *eoff, const int32_t *stok, const float *sw,
+                          const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
+                          size_t scratch_bytes, moe_stream_t stream);
+
 /*
  * moe_combine -- sum each token's expert outputs in the fixed top-k order
  * ([P3] s.3: the same per-token top-k summation order gives bit-identical
@@ -244,6 +292,15 @@ int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, 
 int moe_forward(const void *x, const int32_t *ids, const float *w, const void *w_gate,
                 const void *w_up, const void *w_down, int dtype, int T, int K, int E, int d, int f,
                 int tm, void *workspace, size_t ws_bytes, float *out, moe_stream_t stream);
+
+/*
+ * moe_forward_packed -- moe_forward with packed expert weights (see
+ * moe_pack_weights); same workspace, results (bit for bit) and errors.
+ */
+int moe_forward_packed(const void *x, const int32_t *ids, const float *w, const void *pw_gate,
+                       const void *pw_up, const void *pw_down, int dtype, int T, int K, int E,
+                       int d, int f, int tm, void *workspace, size_t ws_bytes, float *out,
+                       moe_stream_t stream);
 
 /* Byte offsets of moe_forward's intermediates inside the workspace (host only),
  * so that a caller can inspect them after a call. */
@@ -300,6 +357,14 @@ int moe_forward_timed(const void *x, const int32_t *ids, const float *w, const v
  */
 int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
                     moe_stream_t stream);
+
+/* moe_forward_packed with an event pair recorded around every kernel into
+ * `timer` (NULL: identical to moe_forward_packed). */
+int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,
+                             const void *pw_gate, const void *pw_up, const void *pw_down,
+                             int dtype, int T, int K, int E, int d, int f, int tm,
+                             void *workspace, size_t ws_bytes, float *out, moe_stream_t stream,
+                             moe_timer_t *timer);
 
 /* Static description of a status code. */
 const char *moe_status_str(int status);

@@ -20,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
 
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
+MOE_W_GATE_UP, MOE_W_DOWN = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}
 META_FIELDS = ("nent", "nblk", "nr", "nt", "nactive", "maxcnt", "nskip", "nbad", "tm", "E", "K")
 META_N = 11
@@ -67,6 +68,13 @@ _SIGS = {
     "moe_timer_destroy": [P],
     "moe_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
     "moe_stream_read": [P, SZ, P, I32, P],
+    "moe_packed_weight_bytes": [I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_pack_weights": [P, I32, I32, I32, I32, I32, P, SZ, P],
+    "moe_expert_ffn_packed": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ,
+                              P],
+    "moe_forward_packed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P],
+    "moe_forward_packed_timed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P,
+                                 P],
 }
 
 EXPORTS = tuple(_SIGS) + ("moe_status_str",)
@@ -181,6 +189,44 @@ def moe_gather(x, dtype, T, d, stok, meta, max_rows, xs, stream=None):
                                           _stream(stream)))
 
 
+def moe_packed_weight_bytes(E: int, d: int, f: int, dtype: int, kind: int) -> int:
+    v = ctypes.c_size_t()
+    _check("moe_packed_weight_bytes",
+           lib().moe_packed_weight_bytes(E, d, f, dtype, kind, ctypes.byref(v)))
+    return v.value
+
+
+def moe_pack_weights(w, kind: int, packed=None, stream=None):
+    """Pack one set of expert matrices (W_gate/W_up [E, d, f] with kind
+    MOE_W_GATE_UP, W_down [E, f, d] with MOE_W_DOWN); returns the packed bytes."""
+    E = w.shape[0]
+    d, f = (w.shape[1], w.shape[2]) if kind == MOE_W_GATE_UP else (w.shape[2], w.shape[1])
+    dtype = DTYPE_OF[w.dtype]
+    need = moe_packed_weight_bytes(E, d, f, dtype, kind)
+    if packed is None:
+        packed = torch.empty(need, dtype=torch.uint8, device=w.device)
+    _check("moe_pack_weights", lib().moe_pack_weights(
+        _dev(w, "w"), dtype, E, d, f, kind, _dev(packed, "packed"),
+        packed.numel() * packed.element_size(), _stream(stream)))
+    return packed
+
+
+def pack(w_gate, w_up, w_down, stream=None) -> dict:
+    """The three packed matrix sets of a layer, keyed gate / up / down."""
+    return {"gate": moe_pack_weights(w_gate, MOE_W_GATE_UP, stream=stream),
+            "up": moe_pack_weights(w_up, MOE_W_GATE_UP, stream=stream),
+            "down": moe_pack_weights(w_down, MOE_W_DOWN, stream=stream)}
+
+
+def moe_expert_ffn_packed(xs, pw_gate, pw_up, pw_down, dtype, E, d, f, tm, eoff, stok, sw, meta,
+                          max_rows, h, y, scratch, stream=None):
+    _check("moe_expert_ffn_packed", lib().moe_expert_ffn_packed(
+        _dev(xs, "xs"), _dev(pw_gate, "pw_gate"), _dev(pw_up, "pw_up"), _dev(pw_down, "pw_down"),
+        dtype, E, d, f, tm, _dev(eoff, "eoff"), _dev(stok, "stok"), _dev(sw, "sw"),
+        _dev(meta, "meta"), max_rows, _dev(h, "h"), _dev(y, "y"), _dev(scratch, "scratch"),
+        scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
 def moe_expert_ffn(xs, w_gate, w_up, w_down, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows,
                    h, y, scratch, stream=None):
     _check("moe_expert_ffn", lib().moe_expert_ffn(
@@ -196,15 +242,17 @@ def moe_combine(y, max_rows, pos, T, K, d, out, stream=None):
 
 
 def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace, out,
-                stream=None, timer=None):
+                stream=None, timer=None, packed: bool = False):
+    """packed=True: w_gate / w_up / w_down are packed matrix sets (moe_pack_weights)."""
     args = (_dev(x, "x"), _dev(ids, "ids"), _dev(w, "w"), _dev(w_gate, "w_gate"),
             _dev(w_up, "w_up"), _dev(w_down, "w_down"), dtype, T, K, E, d, f, tm,
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
             _dev(out, "out"), _stream(stream))
+    name = "moe_forward_packed" if packed else "moe_forward"
     if timer is None:
-        _check("moe_forward", lib().moe_forward(*args))
+        _check(name, getattr(lib(), name)(*args))
     else:
-        _check("moe_forward_timed", lib().moe_forward_timed(*args, timer.handle))
+        _check(name + "_timed", getattr(lib(), name + "_timed")(*args, timer.handle))
 
 
 class Timer:
@@ -274,8 +322,10 @@ def plan(ids, w, E: int, tm: int = 16, stream=None) -> dict:
 
 
 def forward(x, ids, w, w_gate, w_up, w_down, tm: int = 16, workspace=None, out=None, stream=None,
-            timer=None):
-    """One routed MoE layer on GPU tensors; returns (out [T, d] fp32, workspace)."""
+            timer=None, packed=None):
+    """One routed MoE layer on GPU tensors; returns (out [T, d] fp32, workspace).
+    packed: optional dict of packed matrix sets (see pack()); the layer then reads
+    those instead of w_gate / w_up / w_down, which still give the shapes."""
     T, d = x.shape
     K = ids.shape[1]
     E, _, f = w_gate.shape
@@ -285,6 +335,10 @@ def forward(x, ids, w, w_gate, w_up, w_down, tm: int = 16, workspace=None, out=N
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty((T, d), dtype=torch.float32, device=x.device)
-    moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace, out, stream,
-                timer)
+    if packed is not None:
+        moe_forward(x, ids, w, packed["gate"], packed["up"], packed["down"], dtype, T, K, E, d, f,
+                    tm, workspace, out, stream, timer, packed=True)
+    else:
+        moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace, out,
+                    stream, timer)
     return out, workspace

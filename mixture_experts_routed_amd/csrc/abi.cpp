@@ -169,7 +169,7 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
              int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
              const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
              size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr, bool have_items = false,
-             const void *x = nullptr, int T = 0)
+             const void *x = nullptr, int T = 0, bool packed = false)
 {
     const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                              y, scratch, scratch_bytes);
@@ -183,14 +183,15 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
     {
         Rec r(tmr, s, MOE_STAGE_GATEUP);
         const hipError_t e =
-            x ? moe::launch_gateup_gathered(z, dtype, x, T, stok, wg, wu, d, f, meta, scratch, h,
-                                            s)
-              : moe::launch_gateup(z, dtype, xs, stok, wg, wu, d, f, meta, scratch, h, s);
+            x ? moe::launch_gateup_gathered(z, dtype, packed, x, T, stok, wg, wu, d, f, meta,
+                                            scratch, h, s)
+              : moe::launch_gateup(z, dtype, packed, xs, stok, wg, wu, d, f, meta, scratch, h, s);
         if (e != hipSuccess) return MOE_EHIP;
     }
     {
         Rec r(tmr, s, MOE_STAGE_DOWN);
-        if (moe::launch_down(z, dtype, h, wd, d, f, stok, sw, meta, scratch, y, s) != hipSuccess)
+        if (moe::launch_down(z, dtype, packed, h, wd, d, f, stok, sw, meta, scratch, y, s) !=
+            hipSuccess)
             return MOE_EHIP;
     }
     return MOE_OK;
@@ -239,7 +240,7 @@ int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forwar
 
 int forward_impl(const void *x, const int32_t *ids, const float *w, const void *wg, const void *wu,
                  const void *wd, int dtype, int T, int K, int E, int d, int f, int tm, void *ws,
-                 size_t ws_bytes, float *out, hipStream_t s, moe_timer_t *tmr)
+                 size_t ws_bytes, float *out, hipStream_t s, moe_timer_t *tmr, bool packed = false)
 {
     moe_forward_layout_t L;
     moe_plan_sizes_t z;
@@ -267,7 +268,7 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
                   moe::ffn_shape(E, tm, z.max_rows, d, f, dtype).scratch_bytes, s, tmr, items,
-                  fused_gather ? x : nullptr, T);
+                  fused_gather ? x : nullptr, T, packed);
     if (rc != MOE_OK) return rc;
     return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);
 }
@@ -339,6 +340,62 @@ int moe_expert_ffn(const void *xs, const void *w_gate, const void *w_up, const v
 {
     return ffn_impl(xs, w_gate, w_up, w_down, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                     y, scratch, scratch_bytes, as_stream(stream), nullptr);
+}
+
+int moe_packed_weight_bytes(int E, int d, int f, int dtype, int kind, size_t *bytes)
+{
+    if (!bytes || E < 1 || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 || f % 8 ||
+        (kind != MOE_W_GATE_UP && kind != MOE_W_DOWN))
+        return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    const bool gu = kind == MOE_W_GATE_UP;
+    *bytes = moe::packed_weight_bytes(E, gu ? d : f, gu ? f : d, gu, dtype);
+    return MOE_OK;
+}
+
+int moe_pack_weights(const void *w, int dtype, int E, int d, int f, int kind, void *packed,
+                     size_t packed_bytes, moe_stream_t stream)
+{
+    size_t need = 0;
+    const int rc = moe_packed_weight_bytes(E, d, f, dtype, kind, &need);
+    if (rc != MOE_OK) return rc;
+    if (!aligned(w, 16) || !aligned(packed, 16) || packed_bytes < need) return MOE_EINVAL;
+    if ((int64_t)d * f * elem_bytes(dtype) > ((int64_t)1 << 31)) return MOE_EINVAL;
+    const bool gu = kind == MOE_W_GATE_UP;
+    if (moe::launch_pack(dtype, w, E, gu ? d : f, gu ? f : d, gu, packed, as_stream(stream)) !=
+        hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
+}
+
+int moe_expert_ffn_packed(const void *xs, const void *pw_gate, const void *pw_up,
+                          const void *pw_down, int dtype, int E, int d, int f, int tm,
+                          const int32_t *eoff, const int32_t *stok, const float *sw,
+                          const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
+                          size_t scratch_bytes, moe_stream_t stream)
+{
+    return ffn_impl(xs, pw_gate, pw_up, pw_down, dtype, E, d, f, tm, eoff, stok, sw, meta,
+                    max_rows, h, y, scratch, scratch_bytes, as_stream(stream), nullptr, false,
+                    nullptr, 0, true);
+}
+
+int moe_forward_packed(const void *x, const int32_t *ids, const float *w, const void *pw_gate,
+                       const void *pw_up, const void *pw_down, int dtype, int T, int K, int E,
+                       int d, int f, int tm, void *workspace, size_t ws_bytes, float *out,
+                       moe_stream_t stream)
+{
+    return forward_impl(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, E, d, f, tm, workspace,
+                        ws_bytes, out, as_stream(stream), nullptr, true);
+}
+
+int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,
+                             const void *pw_gate, const void *pw_up, const void *pw_down,
+                             int dtype, int T, int K, int E, int d, int f, int tm,
+                             void *workspace, size_t ws_bytes, float *out, moe_stream_t stream,
+                             moe_timer_t *timer)
+{
+    return forward_impl(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, E, d, f, tm, workspace,
+                        ws_bytes, out, as_stream(stream), timer, true);
 }
 
 int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,

@@ -46,6 +46,93 @@ constexpr int kNpl = 4;                 // columns per lane and B stream
 
 int ffn_rows_per_item() { return kItemRows; }
 
+// Packed weight layout (written once by k_pack, read by the GEMMs with
+// PACKED): a matrix [E][Kd][N] becomes, per expert, column group g (4 slices
+// of 64*m columns), K-step s, wave slice w and stream m (gate/up: m = 1 stream
+// of 64 columns; down: m = 2 halves of 64 columns), a 4 KB tile of 4 x 64
+// 16-byte words, word [c][lane] = what MFMA lane `lane` takes as its c-th B
+// operand of the step: 16-bit types: the 8 K-values 32s + 8*(lane>>4) + i of
+// column (4g+w)*64m + 64*stream + 4*(lane&15) + c; fp32: 4 columns
+// (4g+w)*64m + 64*stream + 4*(lane&15) .. +3 of K-row 16s + 4*(lane>>4) + c.
+// Outside [0,Kd) x [0,N) the words hold zeros. A workgroup's K range of one
+// column group is then one contiguous run of 16 KB (x m) steps.
+struct PackedGeom {
+    int gs, nst, m;       // column groups, K-steps, streams
+    uint32_t step_bytes;  // bytes of one K-step of one column group
+};
+
+__host__ __device__ inline PackedGeom packed_geom(int Kd, int N, bool gateup, int es)
+{
+    PackedGeom z;
+    z.m = gateup ? 1 : 2;
+    const int kstep = es == 2 ? 32 : 16;
+    z.gs = (N + 256 * z.m - 1) / (256 * z.m);
+    z.nst = (Kd + kstep - 1) / kstep;
+    z.step_bytes = 16384u * (uint32_t)z.m;
+    return z;
+}
+
+size_t packed_weight_bytes(int E, int Kd, int N, bool gateup, int dtype)
+{
+    const PackedGeom z = packed_geom(Kd, N, gateup, dtype == 0 ? 4 : 2);
+    return (size_t)E * z.gs * z.nst * z.step_bytes;
+}
+
+// One 16-byte word of the packed layout per thread (grid-stride); U is the
+// raw element (uint16_t for f16/bf16, uint32_t for fp32): bits are copied.
+template <typename U>
+__global__ __launch_bounds__(256) void k_pack(const U *__restrict__ src, int Kd, int N, int gs,
+                                              int nst, int nm, uint4 *__restrict__ dst,
+                                              size_t total)
+{
+    for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * 256) {
+        const int l = (int)(idx & 63), c = (int)((idx >> 6) & 3);
+        size_t t = idx >> 8;
+        const int m = (int)(t % nm);
+        t /= nm;
+        const int w = (int)(t & 3);
+        t >>= 2;
+        const int s = (int)(t % nst);
+        t /= nst;
+        const int g = (int)(t % gs);
+        const size_t e = t / gs;
+        const int n0 = (4 * g + w) * 64 * nm + 64 * m + 4 * (l & 15);
+        auto val = [&](int k, int n) -> uint32_t {
+            return (k < Kd && n < N) ? (uint32_t)src[(e * Kd + k) * (size_t)N + n] : 0u;
+        };
+        uint32_t o[4];
+        if constexpr (sizeof(U) == 2) {
+            const int n = n0 + c, k0 = 32 * s + 8 * (l >> 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = val(k0 + 2 * q, n) | (val(k0 + 2 * q + 1, n) << 16);
+        } else {
+            const int k = 16 * s + 4 * (l >> 4) + c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = val(k, n0 + q);
+        }
+        dst[idx] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+hipError_t launch_pack(int dtype, const void *src, int E, int Kd, int N, bool gateup, void *dst,
+                       hipStream_t s)
+{
+    const PackedGeom z = packed_geom(Kd, N, gateup, dtype == 0 ? 4 : 2);
+    const size_t total = (size_t)E * z.gs * z.nst * z.step_bytes / 16;
+    const size_t want = (total + 255) / 256;
+    const unsigned blocks = (unsigned)(want < (1u << 18) ? want : (1u << 18));
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_pack<uint32_t>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint32_t *>(src), Kd, N, z.gs, z.nst, z.m,
+                           static_cast<uint4 *>(dst), total);
+    else
+        hipLaunchKernelGGL(k_pack<uint16_t>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(src), Kd, N, z.gs, z.nst, z.m,
+                           static_cast<uint4 *>(dst), total);
+    return hipGetLastError();
+}
+
 // Items are ceil(cnt_e / 64) per active expert, so their number is at most
 // (active experts) + (entries beyond one per active expert) / 64; with rows
 // padded to tm this is bounded from max_rows as below.
@@ -395,7 +482,7 @@ constexpr int kLdsU4 = 2 * tall_buf_u4(2) > 2 * kATileU4 ? 2 * tall_buf_u4(2) : 
 // GATHERED (gate/up only): A is the token activation x [a_rows][Kd] and row r
 // of the item reads x[stok[r]] -- the gather fused into the A-tile loads.
 // The K range is [kb, ke) (a split of the reduction, or all of it).
-template <typename T, bool GATEUP, bool GATHERED, int NMT>
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, int NMT>
 __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it, int slice,
                                            int kb, int ke, int split, uint4 *__restrict__ a_lds,
                                            float2 *__restrict__ rinfo)
@@ -425,18 +512,41 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
 
     // operand ranges: this expert's weight rows [kb, ke) (empty for a surplus
     // slice: its loads return zeros without memory traffic), this item's rows
-    const size_t wofs = (size_t)it.expert * Kd * N + (size_t)kb * N;
-    const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
-    const uint32_t wbytes = slice_ok ? kbytes : 0u;
-    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B0 + wofs, wbytes);
-    // ((ke-kb)*N >= 8*8 >= HALF, so the second range never underflows;
-    // readfirstlane keeps the wave-uniform value in an SGPR)
-    const uint32_t wbytes1 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(slice_ok ? kbytes - (uint32_t)(HALF * ES) : 0u));
-    const __amdgpu_buffer_rsrc_t rb1 =
-        GATEUP ? make_rsrc(B1 + wofs, wbytes) : make_rsrc(B0 + wofs + HALF, wbytes1);
-    const uint32_t rowb = (uint32_t)N * ES;  // bytes per weight row
-    const uint32_t vcol = (uint32_t)col * ES;
+    __amdgpu_buffer_rsrc_t rb0, rb1;
+    uint32_t vcol, rowb, bstep;  // lane offset, B row stride, B bytes per K-step
+    if constexpr (PACKED) {
+        // this wavefront's tiles (g, s, w, m) for s in [s0, s1): 4 KB each,
+        // one K-step apart (16 KB x streams)
+        const int g = slice >> 2, w = slice & 3;
+        const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
+        const int s0 = kb / KSTEP, s1 = (ke + KSTEP - 1) / KSTEP;
+        const size_t tb = ((((size_t)it.expert * z.gs + g) * z.nst + s0) * 4 + w) * z.m * 4096;
+        const uint32_t span = (uint32_t)(s1 - s0) * z.step_bytes;
+        const uint32_t r0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(slice_ok ? span - (uint32_t)(w * z.m) * 4096u : 0u));
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(slice_ok ? span - (uint32_t)(w * z.m + z.m - 1) * 4096u : 0u));
+        const char *b0c = static_cast<const char *>(p.B0);
+        rb0 = make_rsrc(b0c + tb, r0);
+        rb1 = GATEUP ? make_rsrc(static_cast<const char *>(p.B1) + tb, r0)
+                     : make_rsrc(b0c + tb + 4096, r1);
+        vcol = (uint32_t)lane * 16;
+        rowb = 1024;  // between fragments c of one lane
+        bstep = z.step_bytes;
+    } else {
+        const size_t wofs = (size_t)it.expert * Kd * N + (size_t)kb * N;
+        const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
+        const uint32_t wbytes = slice_ok ? kbytes : 0u;
+        rb0 = make_rsrc(B0 + wofs, wbytes);
+        // ((ke-kb)*N >= 8*8 >= HALF, so the second range never underflows;
+        // readfirstlane keeps the wave-uniform value in an SGPR)
+        const uint32_t wbytes1 = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(slice_ok ? kbytes - (uint32_t)(HALF * ES) : 0u));
+        rb1 = GATEUP ? make_rsrc(B1 + wofs, wbytes) : make_rsrc(B0 + wofs + HALF, wbytes1);
+        rowb = (uint32_t)N * ES;  // bytes per weight row
+        vcol = (uint32_t)col * ES;
+        bstep = (uint32_t)KSTEP * rowb;
+    }
     // this thread's share of the A tile: row tid/4, 16-byte chunk tid%4
     const int arow = tid >> 2, achunk = (tid & 3) * (16 / ES);
     __amdgpu_buffer_rsrc_t ra;
@@ -465,17 +575,21 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
 #pragma unroll
             for (int c = 0; c < NPL; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    // packed: 4 fragments (fp32: 4 rows) of 16 bytes per stream and step
+    constexpr int NB = PACKED ? 4 : KR;
+    constexpr int LBB = PACKED ? 16 : LB;
+    typedef typename Ld<LBB>::type BT;
     struct Stage {
-        RowT b[NMAT][KR];
+        BT b[NMAT][NB];
         uint4 a;
     };
     auto load = [&](Stage &st, int k0) {
-        const int kk = k0 + KR * kg;
-        const uint32_t vb = vcol + (uint32_t)(kk - kb) * rowb;
+        const uint32_t vb = PACKED ? vcol + (uint32_t)((k0 - kb) / KSTEP) * bstep
+                                   : vcol + (uint32_t)(k0 + KR * kg - kb) * rowb;
 #pragma unroll
-        for (int i = 0; i < KR; ++i) st.b[0][i] = Ld<LB, kNT>::run(rb0, vb, (uint32_t)i * rowb);
+        for (int i = 0; i < NB; ++i) st.b[0][i] = Ld<LBB, kNT>::run(rb0, vb, (uint32_t)i * rowb);
 #pragma unroll
-        for (int i = 0; i < KR; ++i) st.b[1][i] = Ld<LB, kNT>::run(rb1, vb, (uint32_t)i * rowb);
+        for (int i = 0; i < NB; ++i) st.b[1][i] = Ld<LBB, kNT>::run(rb1, vb, (uint32_t)i * rowb);
         // K past the range: the weights read as zero; zero A too so that no
         // non-finite value of a neighbouring row can leak in as 0 * inf.
         const int ka = k0 + achunk;
@@ -494,7 +608,11 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
             for (int c = 0; c < NPL; ++c) {
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m) {
-                    const uint4 fb = column_of_rows(st.b[m], c);
+                    uint4 fb;
+                    if constexpr (PACKED)
+                        fb = st.b[m][c];
+                    else
+                        fb = column_of_rows(st.b[m], c);
 #pragma unroll
                     for (int mt = 0; mt < NMT; ++mt)
                         acc[m][mt][c] = Elt<T>::mfma(af[mt], fb, acc[m][mt][c]);
@@ -549,7 +667,7 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
 // Every wavefront computes 4 m-tiles (a short last item computes zero rows).
 // The weight loads keep the default cache policy here: the other runs of the
 // same expert read the same tile, often while it is still in L2.
-template <typename T, bool GATEUP, bool GATHERED, int R>
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, int R>
 __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__restrict__ items,
                                            int i0, int nitems, int g, int j, int kb, int ke,
                                            int split, uint4 *__restrict__ lds,
@@ -596,16 +714,38 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
     const int plu = C == 1 ? ((tid >> 1) & 63) : lane;
     const int hh = C == 1 ? (tid & 1) : 0;
     const int pslice = 4 * g + C * j + pcs;
-    const size_t wofs = (size_t)expert * Kd * N + (size_t)kb * N;
-    const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
-    // pm and pslice are wave-uniform: keep the range and base in SGPRs
-    const uint32_t pbytes = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(pslice * SW >= N ? 0u : (GATEUP || pm == 0) ? kbytes : kbytes - (uint32_t)(HALF * ES)));
-    const T *pbase = GATEUP ? (pm ? B1 + wofs : B0 + wofs) : B0 + wofs + pm * HALF;
-    const __amdgpu_buffer_rsrc_t rbp = make_rsrc(pbase, pbytes);
-    const uint32_t rowb = (uint32_t)N * ES;
-    const uint32_t vpb = (uint32_t)(pslice * SW + NPL * (plu & 15)) * ES +
-                         (uint32_t)(KR * (plu >> 4) + RP * hh) * rowb;
+    // packed: a producer thread copies 4/H whole fragments (fp32: rows) of its unit
+    constexpr int PNB = PACKED ? 4 / H : RP;
+    __amdgpu_buffer_rsrc_t rbp;
+    uint32_t rowb, vpb, bstep;
+    if constexpr (PACKED) {
+        const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
+        const int s0 = kb / KSTEP, s1 = (ke + KSTEP - 1) / KSTEP;
+        const int wp = C * j + pcs, mm = GATEUP ? 0 : pm;  // tile slot in the group
+        const size_t tb =
+            (((((size_t)expert * z.gs + g) * z.nst + s0) * 4 + wp) * z.m + mm) * 4096;
+        const uint32_t span = (uint32_t)(s1 - s0) * z.step_bytes;
+        const uint32_t pbytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(pslice * SW >= N ? 0u : span - (uint32_t)(wp * z.m + mm) * 4096u));
+        const char *bb = static_cast<const char *>(GATEUP && pm ? p.B1 : p.B0);
+        rbp = make_rsrc(bb + tb, pbytes);
+        rowb = 1024;
+        vpb = (uint32_t)(hh * PNB) * 1024 + (uint32_t)plu * 16;
+        bstep = z.step_bytes;
+    } else {
+        const size_t wofs = (size_t)expert * Kd * N + (size_t)kb * N;
+        const uint32_t kbytes = (uint32_t)((size_t)(ke - kb) * N * ES);
+        // pm and pslice are wave-uniform: keep the range and base in SGPRs
+        const uint32_t pbytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)(
+            pslice * SW >= N ? 0u
+                             : (GATEUP || pm == 0) ? kbytes : kbytes - (uint32_t)(HALF * ES)));
+        const T *pbase = GATEUP ? (pm ? B1 + wofs : B0 + wofs) : B0 + wofs + pm * HALF;
+        rbp = make_rsrc(pbase, pbytes);
+        rowb = (uint32_t)N * ES;
+        vpb = (uint32_t)(pslice * SW + NPL * (plu & 15)) * ES +
+              (uint32_t)(KR * (plu >> 4) + RP * hh) * rowb;
+        bstep = (uint32_t)KSTEP * rowb;
+    }
 
     // A: 4 m-tiles of this wavefront's item; lane row 16*mt + nq, K chunk kg
     __amdgpu_buffer_rsrc_t ra;
@@ -635,14 +775,16 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
 #pragma unroll
             for (int c = 0; c < NPL; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    constexpr int LBB = PACKED ? 16 : LB;
+    typedef typename Ld<LBB>::type BT;
     struct Stage {
-        RowT b[RP];
+        BT b[PNB];
         uint4 a[NMT];
     };
     auto load = [&](Stage &st, int k0) {
-        const uint32_t vb = vpb + (uint32_t)(k0 - kb) * rowb;
+        const uint32_t vb = vpb + (uint32_t)((k0 - kb) / KSTEP) * bstep;
 #pragma unroll
-        for (int i = 0; i < RP; ++i) st.b[i] = Ld<LB>::run(rbp, vb, (uint32_t)i * rowb);
+        for (int i = 0; i < PNB; ++i) st.b[i] = Ld<LBB>::run(rbp, vb, (uint32_t)i * rowb);
         const int ka = k0 + KR * kg;
         const uint32_t am = ka < ke ? 0xffffffffu : 0u;
 #pragma unroll
@@ -653,7 +795,10 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
     auto frag = [&](int s, int m, int q, int l) { return ((s * NMAT + m) * 4 + q) * 64 + l; };
     auto compute = [&](const Stage &st, int step) {
         uint4 *buf = lds + (step & 1) * BUF;
-        if constexpr (ES == 2) {
+        if constexpr (PACKED) {
+#pragma unroll
+            for (int i = 0; i < PNB; ++i) buf[frag(pcs, pm, PNB * hh + i, plu)] = st.b[i];
+        } else if constexpr (ES == 2) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 uint32_t o[RP / 2];
@@ -715,7 +860,7 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
 }
 
 // One workgroup per (work item, group of 4 column slices, K split).
-template <typename T, bool GATEUP, bool GATHERED>
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
                                                         const int32_t *__restrict__ ctl,
                                                         const WorkItem *__restrict__ items)
@@ -737,23 +882,23 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     const WorkItem it = items[i];
     const int run = it.run & 0xff, j = (it.run >> 8) & 0xff;
     if (run == 4 && j < 4 && i >= j) {
-        tall_cells<T, GATEUP, GATHERED, 4>(p, items, i - j, nitems, g, j, kb, ke, split, lds,
-                                           rinfo);
+        tall_cells<T, GATEUP, GATHERED, PACKED, 4>(p, items, i - j, nitems, g, j, kb, ke, split,
+                                                   lds, rinfo);
         return;
     }
     if (run == 2 && j < 2 && i >= j) {
-        tall_cells<T, GATEUP, GATHERED, 2>(p, items, i - j, nitems, g, j, kb, ke, split, lds,
-                                           rinfo);
+        tall_cells<T, GATEUP, GATHERED, PACKED, 2>(p, items, i - j, nitems, g, j, kb, ke, split,
+                                                   lds, rinfo);
         return;
     }
     // wave-uniform by construction, so the buffer descriptors live in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = g * kWavesPerBlock + wave;
     switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wide_cells<T, GATEUP, GATHERED, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 2: wide_cells<T, GATEUP, GATHERED, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 3: wide_cells<T, GATEUP, GATHERED, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    default: wide_cells<T, GATEUP, GATHERED, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    default: wide_cells<T, GATEUP, GATHERED, PACKED, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
     }
 }
 
@@ -853,7 +998,7 @@ GemmArgs gemm_args(const FfnShape &z, const void *scratch, bool gateup)
 
 unsigned reduce_blocks(int64_t rows, int N) { return (unsigned)((rows * (N / 4) + 255) / 256); }
 
-template <typename T>
+template <typename T, bool PACKED>
 hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
                     const int32_t *stok, const void *wg, const void *wu, int d, int f,
                     const int32_t *meta, const void *scratch, void *h, hipStream_t s)
@@ -869,10 +1014,10 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     p.N = f;
     const dim3 grid((unsigned)z.blocks_gu);
     if (gathered)  // rows gathered from x through stok
-        hipLaunchKernelGGL((k_expert_gemm<T, true, true>), grid, dim3(256), 0, s, p,
+        hipLaunchKernelGGL((k_expert_gemm<T, true, true, PACKED>), grid, dim3(256), 0, s, p,
                            ctl_of(scratch), items_of(scratch));
     else
-        hipLaunchKernelGGL((k_expert_gemm<T, true, false>), grid, dim3(256), 0, s, p,
+        hipLaunchKernelGGL((k_expert_gemm<T, true, false, PACKED>), grid, dim3(256), 0, s, p,
                            ctl_of(scratch), items_of(scratch));
     if (z.split_gu > 1)
         hipLaunchKernelGGL(k_reduce_gateup<T>, dim3(reduce_blocks(z.max_rows, f)), dim3(256), 0, s,
@@ -881,7 +1026,7 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool PACKED>
 hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f,
                   const int32_t *stok, const float *sw, const int32_t *meta, const void *scratch,
                   float *y, hipStream_t s)
@@ -894,43 +1039,60 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
     p.out = y;
     p.Kd = f;
     p.N = d;
-    hipLaunchKernelGGL((k_expert_gemm<T, false, false>), dim3((unsigned)z.blocks_dn), dim3(256),
-                       0, s, p, ctl_of(scratch), items_of(scratch));
+    hipLaunchKernelGGL((k_expert_gemm<T, false, false, PACKED>), dim3((unsigned)z.blocks_dn),
+                       dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch));
     if (z.split_dn > 1)
         hipLaunchKernelGGL(k_reduce_down, dim3(reduce_blocks(z.max_rows, d)), dim3(256), 0, s,
                            p.part, p.plane, p.nsplit, d, stok, sw, meta, z.max_rows, y);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const int32_t *stok,
-                         const void *wg, const void *wu, int d, int f, const int32_t *meta,
-                         const void *scratch, void *h, hipStream_t s)
+template <typename T>
+hipError_t gateup_any(const FfnShape &z, bool packed, const void *a, int a_rows, bool gathered,
+                      const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                      const int32_t *meta, const void *scratch, void *h, hipStream_t s)
 {
-    if (dtype == 1)
-        return gateup_t<_Float16>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
-    if (dtype == 2)
-        return gateup_t<__bf16>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
-    return gateup_t<float>(z, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+    return packed ? gateup_t<T, true>(z, a, a_rows, gathered, stok, wg, wu, d, f, meta, scratch, h, s)
+                  : gateup_t<T, false>(z, a, a_rows, gathered, stok, wg, wu, d, f, meta, scratch, h,
+                                       s);
 }
 
-hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,
+}  // namespace
+
+hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *xs,
+                         const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                         const int32_t *meta, const void *scratch, void *h, hipStream_t s)
+{
+    if (dtype == 1)
+        return gateup_any<_Float16>(z, packed, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2)
+        return gateup_any<__bf16>(z, packed, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_any<float>(z, packed, xs, 0, false, stok, wg, wu, d, f, meta, scratch, h, s);
+}
+
+hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
                                   const int32_t *meta, const void *scratch, void *h, hipStream_t s)
 {
-    if (dtype == 1) return gateup_t<_Float16>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
-    if (dtype == 2) return gateup_t<__bf16>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
-    return gateup_t<float>(z, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 1)
+        return gateup_any<_Float16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+    if (dtype == 2)
+        return gateup_any<__bf16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+    return gateup_any<float>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
 }
 
-hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *wd, int d, int f,
-                       const int32_t *stok, const float *sw, const int32_t *meta,
+hipError_t launch_down(const FfnShape &z, int dtype, bool packed, const void *h, const void *wd,
+                       int d, int f, const int32_t *stok, const float *sw, const int32_t *meta,
                        const void *scratch, float *y, hipStream_t s)
 {
-    if (dtype == 1) return down_t<_Float16>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
-    if (dtype == 2) return down_t<__bf16>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
-    return down_t<float>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+    if (dtype == 1)
+        return packed ? down_t<_Float16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
+                      : down_t<_Float16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+    if (dtype == 2)
+        return packed ? down_t<__bf16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
+                      : down_t<__bf16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+    return packed ? down_t<float, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
+                  : down_t<float, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
 }
 
 }  // namespace moe

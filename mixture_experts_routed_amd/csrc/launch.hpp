@@ -57,17 +57,24 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype);
 
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, hipStream_t s);
-hipError_t launch_gateup(const FfnShape &z, int dtype, const void *xs, const int32_t *stok,
-                         const void *wg, const void *wu, int d, int f, const int32_t *meta,
-                         const void *scratch, void *h, hipStream_t s);
+hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *xs,
+                         const int32_t *stok, const void *wg, const void *wu, int d, int f,
+                         const int32_t *meta, const void *scratch, void *h, hipStream_t s);
 // gate/up reading row r straight from x[stok[r]] (the gather fused into the
 // A-tile loads); x must be smaller than 2 GiB.
-hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, const void *x, int T,
+hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
                                   const int32_t *meta, const void *scratch, void *h, hipStream_t s);
-hipError_t launch_down(const FfnShape &z, int dtype, const void *h, const void *wd, int d, int f,
-                       const int32_t *stok, const float *sw, const int32_t *meta,
+hipError_t launch_down(const FfnShape &z, int dtype, bool packed, const void *h, const void *wd,
+                       int d, int f, const int32_t *stok, const float *sw, const int32_t *meta,
                        const void *scratch, float *y, hipStream_t s);
+
+// ---- packed expert weights ----
+// bytes of one packed matrix set: gate/up matrices [E][d][f] (gateup = true,
+// Kd = d, N = f) or the down matrices [E][f][d] (Kd = f, N = d)
+size_t packed_weight_bytes(int E, int Kd, int N, bool gateup, int dtype);
+hipError_t launch_pack(int dtype, const void *src, int E, int Kd, int N, bool gateup, void *dst,
+                       hipStream_t s);
 
 // ---- measurement only ----
 // one streaming read of `bytes` (16-byte words) of src; sink holds sink_words

@@ -97,6 +97,26 @@ def test_gather_combine_ffn_forward_reject_bad_arguments():
                          None) == 1                                   # workspace not 256-aligned
 
 
+def test_packed_weight_sizes_and_rejects():
+    L = abi.lib()
+    v = ctypes.c_size_t()
+    # prefill shape: no padding (f = 768 = 3 x 256 columns, d = 2560 = 80 x 32 K)
+    assert L.moe_packed_weight_bytes(512, 2560, 768, 1, 0, ctypes.byref(v)) == 0
+    assert v.value == 512 * 2560 * 768 * 2
+    assert L.moe_packed_weight_bytes(512, 2560, 768, 1, 1, ctypes.byref(v)) == 0
+    assert v.value == 512 * 2560 * 768 * 2
+    # ragged: columns padded to 256 (gate/up) / 512 (down), K to 32 (16-bit) / 16 (fp32)
+    assert L.moe_packed_weight_bytes(3, 328, 200, 1, 0, ctypes.byref(v)) == 0
+    assert v.value == 3 * 256 * 352 * 2
+    assert L.moe_packed_weight_bytes(3, 328, 200, 0, 1, ctypes.byref(v)) == 0
+    assert v.value == 3 * 512 * 208 * 4
+    assert L.moe_packed_weight_bytes(3, 328, 200, 1, 2, ctypes.byref(v)) == 1   # bad kind
+    assert L.moe_packed_weight_bytes(3, 330, 200, 1, 0, ctypes.byref(v)) == 1   # d % 8
+    assert L.moe_packed_weight_bytes(2000, 64, 64, 1, 0, ctypes.byref(v)) == 2  # E too large
+    assert L.moe_pack_weights(A, 1, 3, 328, 200, 0, A, 10, None) == 1          # small output
+    assert L.moe_pack_weights(A + 8, 1, 3, 328, 200, 0, A, 1 << 30, None) == 1  # misaligned
+
+
 def test_stream_read_rejects_bad_arguments():
     L = abi.lib()
     assert L.moe_stream_read(A + 8, 1 << 20, A, 16, None) == 1   # src not 16-byte aligned

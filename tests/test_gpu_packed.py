@@ -1,0 +1,103 @@
+"""Packed expert weights (moe_pack_weights): the packed layer feeds the matrix
+cores the same operand bits in the same order as the row-major one, so
+moe_forward_packed must equal moe_forward and moe_expert_ffn_packed must equal
+moe_expert_ffn bit for bit, on every launch path (wide and tall cells, K split
+or not, fp32 / fp16 / bf16, ragged d and f). The row-major path is itself
+checked against the oracle in test_gpu_forward / test_gpu_ffn; the prefill
+workload is also checked against the oracle here, through the packed path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, abi, custom, dev, host, make_case, rel_err, say, synth
+from test_gpu_ffn import PATHS as FFN_PATHS
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    synth.CONFIGS["tiny_fp32"],
+    custom("ragged_tails_f16", T=96, d=328, E=12, K=3, f=200, dtype="f16"),
+    custom("ragged_tails_bf16", T=96, d=328, E=12, K=3, f=200, dtype="bf16", x_std=1.0),
+    custom("ragged_tails_f32", T=80, d=136, E=6, K=2, f=72, dtype="f32", x_std=1.0),
+    custom("tm1_no_padding", T=150, d=256, E=10, K=2, f=128, dtype="f16", tm=1),
+] + [c[0] for c in FFN_PATHS]
+
+
+def packed_of(case):
+    return abi.pack(case.d("wg"), case.d("wu"), case.d("wd"))
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_forward_packed_equals_rowmajor(cfg):
+    case = make_case(cfg)
+    say(f"[packed forward] {cfg.name}")
+    x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
+    a, ws = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm)
+    pk = packed_of(case)
+    b, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                       workspace=ws, packed=pk)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    case.drop_device()
+
+
+@pytest.mark.parametrize("cfg", CASES[:5], ids=[c.name for c in CASES[:5]])
+def test_expert_ffn_packed_equals_rowmajor(cfg):
+    case = make_case(cfg)
+    T, K = case.ids.shape
+    p = oracle.plan(case.ids, case.w, cfg.E, cfg.tm)
+    z = abi.moe_plan_sizes(T, K, cfg.E, cfg.tm)
+    R, nr = z.max_rows, len(p["stok"])
+    xs = np.zeros((R, cfg.d), case.x.dtype)
+    xs[:nr] = oracle.gather(case.x, p["stok"])
+    stok = np.full(R, -1, np.int32)
+    stok[:nr] = p["stok"]
+    sw = np.zeros(R, np.float32)
+    sw[:nr] = p["sw"]
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    tdt = abi.TORCH_DTYPE[dt]
+    scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt),
+                          dtype=torch.uint8, device="cuda")
+    args = (dev(p["eoff"]), dev(stok), dev(sw), dev(p["meta"]), R)
+    outs = []
+    pk = packed_of(case)
+    for packed in (False, True):
+        h = torch.zeros((R, cfg.f), dtype=tdt, device="cuda")
+        y = torch.zeros((R, cfg.d), dtype=torch.float32, device="cuda")
+        if packed:
+            abi.moe_expert_ffn_packed(dev(xs, cfg.dtype), pk["gate"], pk["up"], pk["down"], dt,
+                                      cfg.E, cfg.d, cfg.f, cfg.tm, *args, h, y, scratch)
+        else:
+            abi.moe_expert_ffn(dev(xs, cfg.dtype), case.d("wg"), case.d("wu"), case.d("wd"), dt,
+                               cfg.E, cfg.d, cfg.f, cfg.tm, *args, h, y, scratch)
+        torch.cuda.synchronize()
+        outs.append((host(h), host(y)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    case.drop_device()
+
+
+@pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16"])
+def test_forward_packed_full_size(name):
+    """full-size workloads: packed == row-major bitwise, and packed vs the oracle
+    on a sample of tokens"""
+    cfg = synth.CONFIGS[name]
+    case = make_case(cfg)
+    say(f"[packed forward] {name} full size")
+    x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
+    a, ws = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm)
+    got_a = host(a)
+    pk = packed_of(case)
+    b, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                       workspace=ws, packed=pk)
+    got = host(b)
+    assert np.array_equal(got_a.view(np.uint32), got.view(np.uint32))
+    g = np.random.default_rng(cfg.seed)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], g.choice(cfg.T, min(16, cfg.T),
+                                                              replace=False)])).astype(np.int32)
+    ref = oracle.ffn(case.x, case.ids, case.w, case.wg, case.wu, case.wd, cfg.dtype, True,
+                     tokens=toks)
+    assert rel_err(got[toks], ref.astype(np.float32)) <= TOL[cfg.dtype]
+    del pk
+    case.drop_device()
