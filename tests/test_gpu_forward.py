@@ -124,3 +124,36 @@ def test_forward_skipped_entries():
     got, _ = gpu_forward(case, ids, case.w, case.x)
     compare(case, ids, case.w, case.x, got, np.arange(cfg.T, dtype=np.int32))
     assert np.all(got[5] == 0) and not np.any(np.signbit(got[5]))
+
+
+@pytest.mark.parametrize("cfg", [synth.CONFIGS["decode_bf16"], synth.CONFIGS["tiny_fp32"],
+                                 PATHS[0], custom("no_split_f16", T=2048, d=2048, E=64, K=4,
+                                                  f=1024, dtype="f16")],
+                         ids=["decode_bf16_split_both", "tiny_fp32_split_down",
+                              "split_both_bf16", "no_split_f16"])
+def test_forward_equals_the_four_calls(cfg):
+    """moe_forward (one-launch plan, gather fused into gate/up, and, when the
+    down projection is split along K, the combine adding the split partials
+    itself) returns the same bits as moe_plan, moe_gather, moe_expert_ffn and
+    moe_combine called one by one"""
+    case = make_case(cfg)
+    say(f"[forward vs four calls] {cfg.name}")
+    T, K = case.ids.shape
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
+    a, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm)
+    p = abi.plan(ids, w, cfg.E, cfg.tm)
+    R = p["sizes"].max_rows
+    xs = torch.empty((R, cfg.d), dtype=x.dtype, device="cuda")
+    abi.moe_gather(x, dt, T, cfg.d, p["stok"], p["meta"], R, xs)
+    h = torch.empty((R, cfg.f), dtype=x.dtype, device="cuda")
+    y = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt),
+                          dtype=torch.uint8, device="cuda")
+    abi.moe_expert_ffn(xs, case.d("wg"), case.d("wu"), case.d("wd"), dt, cfg.E, cfg.d, cfg.f,
+                       cfg.tm, p["eoff"], p["stok"], p["sw"], p["meta"], R, h, y, scratch)
+    b = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    abi.moe_combine(y, R, p["pos"], T, K, cfg.d, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    case.drop_device()
