@@ -157,3 +157,27 @@ def test_forward_equals_the_four_calls(cfg):
     torch.cuda.synchronize()
     assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
     case.drop_device()
+
+
+def test_forward_activation_of_2gib_gathers_first():
+    """x of 2 GiB (T=131072, d=8192, fp16) is past what one buffer descriptor
+    addresses, so moe_forward gathers the rows first (moe_gather's kernel,
+    64-bit row offsets) and the gate/up projection reads them row-major. A
+    token's output depends only on its own row: sampled tokens get seeded random
+    rows (checked against the oracle), all others zero rows, whose output must
+    be exactly zero."""
+    from gpu_util import Case
+    cfg = custom("x_2gib_f16", T=131072, d=8192, E=4, K=1, f=64, dtype="f16")
+    assert cfg.T * cfg.d * 2 >= 1 << 31
+    ids, w = synth.routing(cfg)
+    toks = sample_tokens(cfg.T, cfg.seed, n=12)
+    x = np.zeros((cfg.T, cfg.d), np.uint16)
+    x[toks] = synth.to_dtype(synth.random_rows(cfg.seed, len(toks), cfg.d, std=0.02), "f16")
+    case = Case(cfg, ids, w, x, synth.expert_weights(cfg, "gate"), synth.expert_weights(cfg, "up"),
+                synth.expert_weights(cfg, "down"))
+    say(f"[forward] {cfg.name}")
+    got, _ = gpu_forward(case, case.ids, case.w, case.x)
+    compare(case, case.ids, case.w, case.x, got, toks)
+    got[toks] = 0.0
+    assert not np.any(got.view(np.uint32))  # +0.0 on every other token
+    case.drop_device()
