@@ -40,6 +40,10 @@ SMALL = [
     custom("skewed_small_bf16", T=400, d=192, E=32, K=4, f=96, dtype="bf16", bias="zipf1.1"),
     custom("single_expert", T=200, d=64, E=1, K=1, f=64, dtype="f32"),
     custom("single_token", T=1, d=512, E=64, K=6, f=256, dtype="f16"),
+    custom("max_experts_f16", T=300, d=64, E=1024, K=8, f=64, dtype="f16"),
+    custom("min_dims_bf16", T=50, d=8, E=4, K=2, f=8, dtype="bf16", x_std=1.0, w_std=0.5),
+    custom("k_equals_e_f32", T=20, d=40, E=6, K=6, f=24, dtype="f32", x_std=1.0),
+    custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
 ]
 
 

@@ -21,6 +21,10 @@ CASES = [
     custom("ragged_tails_bf16", T=96, d=328, E=12, K=3, f=200, dtype="bf16", x_std=1.0),
     custom("ragged_tails_f32", T=80, d=136, E=6, K=2, f=72, dtype="f32", x_std=1.0),
     custom("tm1_no_padding", T=150, d=256, E=10, K=2, f=128, dtype="f16", tm=1),
+    custom("max_experts_f16", T=300, d=64, E=1024, K=8, f=64, dtype="f16"),
+    custom("min_dims_bf16", T=50, d=8, E=4, K=2, f=8, dtype="bf16", x_std=1.0, w_std=0.5),
+    custom("k_equals_e_f32", T=20, d=40, E=6, K=6, f=24, dtype="f32", x_std=1.0),
+    custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
 ] + [c[0] for c in FFN_PATHS]
 
 
