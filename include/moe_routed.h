@@ -202,9 +202,10 @@ int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int
  *      eoff [E+1], stok [max_rows], sw [max_rows], meta [MOE_META_N].
  * Out: h [max_rows][f] (dtype), y [max_rows][d] fp32.
  * scratch: at least moe_ffn_scratch_bytes().
- * Errors: MOE_EINVAL for d or f not positive multiples of 8, bad dtype,
- * NULL/misaligned pointers, small scratch, tm < 1; MOE_EUNSUPPORTED for
- * E > MOE_MAX_EXPERTS; MOE_EHIP on a failed launch.
+ * Errors: MOE_EINVAL for d or f not positive multiples of 8 or above 2^22,
+ * one expert matrix of 2 GiB or more, bad dtype, NULL/misaligned pointers,
+ * small scratch, tm < 1; MOE_EUNSUPPORTED for E > MOE_MAX_EXPERTS; MOE_EHIP on
+ * a failed launch.
  */
 int moe_expert_ffn(const void *xs, const void *w_gate, const void *w_up, const void *w_down,
                    int dtype, int E, int d, int f, int tm, const int32_t *eoff, const int32_t *stok,

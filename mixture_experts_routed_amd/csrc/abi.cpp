@@ -51,8 +51,10 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
         return MOE_EINVAL;
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
     if (max_rows * (int64_t)(d > f ? d : f) > ((int64_t)1 << 40)) return MOE_EINVAL;
-    // one expert matrix is addressed by one buffer descriptor (32-bit offsets)
+    // one expert matrix, and a work item's 64 rows of h or y, are each addressed
+    // by one buffer descriptor (32-bit offsets)
     if ((int64_t)d * f * elem_bytes(dtype) > ((int64_t)1 << 31)) return MOE_EINVAL;
+    if (d > (1 << 22) || f > (1 << 22)) return MOE_EINVAL;
     if (!aligned(xs, 16) || !aligned(wg, 16) || !aligned(wu, 16) || !aligned(wd, 16) ||
         !aligned(h, 16) || !aligned(y, 16) || !aligned(eoff, 4) || !aligned(stok, 4) ||
         !aligned(sw, 4) || !aligned(meta, 4) || !aligned(scratch, 16))

@@ -279,6 +279,18 @@ __device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
     __builtin_nontemporal_store(u2{v.x, v.y}, reinterpret_cast<u2 *>(p));
 }
 
+// Stores of the down projection's y, which the combine reads next: buffer
+// stores with cache policy sc1 only. Measured on the prefill layer against
+// non-temporal stores: the down projection ~15 us and the combine ~7 us faster
+// (its y reads then hit the Infinity Cache). Default-policy stores were slower
+// than both, and sc1 stores of the gate/up output h gained nothing.
+constexpr int kSC1 = 16;
+__device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v)
+{
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kSC1);
+}
+
 // ---- per element type: MFMA and conversion -------------------------------
 template <typename T> struct Elt;
 
@@ -423,17 +435,20 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
                 const float2 ri = rinfo[rl];
                 if (__float_as_int(ri.y) < 0) continue;  // pad rows are never combined
                 const float g = partial ? 1.0f : ri.x;
-                float *Y = partial ? p.part + split * p.plane + row * N + col
-                                   : static_cast<float *>(p.out) + row * N + col;
+                float *P = p.part + split * p.plane + row * N + col;
+                // the item's rows of y, as one descriptor (range-checked stores)
+                const __amdgpu_buffer_rsrc_t ry =
+                    make_rsrc(static_cast<float *>(p.out) + (int64_t)it.row0 * N,
+                              (uint32_t)(it.nrows * N * 4));
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     if (col + m * HALF >= N) continue;
                     const float4 v = make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
                                                  g * acc[m][mt][2][r], g * acc[m][mt][3][r]);
                     if (partial)
-                        *reinterpret_cast<float4 *>(Y + m * HALF) = v;
+                        *reinterpret_cast<float4 *>(P + m * HALF) = v;
                     else
-                        store_nt(reinterpret_cast<float4 *>(Y + m * HALF), v);
+                        store_sc1(ry, (uint32_t)((rl * N + col + m * HALF) * 4), v);
                 }
             }
         }
