@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed (token,expert) rows/sec per MoE layer, T=2048 E=512 top-10; plan us/layer"
 HBM_PEAK_GBS = 8000.0
+# dense matrix-core peaks (TFLOP/s) by element type; fp32 runs on the fp32 MFMA
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -184,6 +186,13 @@ def gateup_bytes(cfg, meta, T):
     es = 2 if cfg.dtype != "f32" else 4
     nactive, nr = int(meta[4]), int(meta[2])
     return 2 * nactive * cfg.d * cfg.f * es + T * cfg.d * es + nr * cfg.f * es
+
+
+def stage_flops(cfg, meta):
+    """Algorithmic matrix FLOPs of the two grouped GEMMs of one moe_forward call, on the rows
+    that hold an entry (tile padding not counted)."""
+    nreal = int(meta[0]) - int(meta[6]) - int(meta[7])
+    return {"gateup": 2 * nreal * cfg.d * 2 * cfg.f, "down": 2 * nreal * cfg.f * cfg.d}
 
 
 def stage_bytes(cfg, meta, T):
@@ -377,6 +386,23 @@ def main():
     gu_bytes = gateup_bytes(cfg, meta, T)
     gu_s = gu_us * 1e-6
     achieved = gu_bytes / gu_s / 1e9
+    flops = stage_flops(cfg, meta)
+    mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    # the gate/up launch is bound by the matrix cores when its arithmetic intensity
+    # (algorithmic FLOPs per algorithmic byte) is above the ridge peak FLOP/s / HBM B/s
+    mfma_bound = flops["gateup"] / gu_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"kernel": "gateup_swiglu", "bound": "mfma",
+                "achieved": flops["gateup"] / gu_s / 1e12, "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": flops["gateup"] / gu_s / 1e12 / mfma_peak, "traffic": None,
+                "hbm_gbs": round(achieved, 1),
+                "algorithmic_flops_per_launch": flops["gateup"],
+                "algorithmic_bytes_per_launch": gu_bytes}
+    else:
+        roof = {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": recorded_traffic("k_expert_gemm/gateup"),
+                "algorithmic_bytes_per_launch": gu_bytes}
     rows = cfg.T * K
     res = {
         "metric": METRIC, "value": rows / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
@@ -405,21 +431,19 @@ def main():
                        if us.get(k)},
         "step_us": step_us,
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
-        "roofline": {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic("k_expert_gemm/gateup"),
-                     "read_probe_gbs": round(read_gbs, 1),
-                     "read_probe_note": "same run: moe_stream_read over 2 GiB (each workgroup "
-                                        "one contiguous chunk, 16-byte non-temporal loads, "
-                                        "no compute) reaches this rate",
-                     "algorithmic_bytes_per_launch": gu_bytes},
+        "stages_tflops": {k: round(v / (us[k] * 1e6), 1) for k, v in flops.items() if us.get(k)},
+        "roofline": dict(roof, read_probe_gbs=round(read_gbs, 1),
+                         read_probe_note="same run: moe_stream_read over 2 GiB (each workgroup "
+                                         "one contiguous chunk, 16-byte non-temporal loads, "
+                                         "no compute) reaches this rate"),
     }
     if args.workload != "prefill_fp16":
         # the headline metric is quoted on the prefill layer; other workloads report
         # their own throughput under a metric name of their own
         res["metric"] = f"routed (token,expert) rows/sec, {cfg.name}"
-        res["roofline"]["note"] = ("algorithmic bytes of the last call's gate/up launch over the "
-                                   "mean gate/up launch time")
+        res["roofline"]["note"] = ("algorithmic %s of the last call's gate/up launch over the "
+                                   "mean gate/up launch time"
+                                   % ("FLOPs (rows holding an entry)" if mfma_bound else "bytes"))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, ids[:T], w[:T], x[:T], args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -188,6 +188,18 @@ int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int
                    int *split_down);
 
 /*
+ * moe_ffn_big_cells -- host only: *on = 1 when, for these sizes, the packed
+ * entry points (moe_expert_ffn_packed, moe_forward_packed) with fp16 or bf16
+ * run each expert's runs of 4 work items (256 rows) of the gate/up projection
+ * on 512-thread workgroups of 256 rows x 128 columns whose operands are staged
+ * in LDS (a separate launch before the other work items), else 0. Used when
+ * the plan bound averages at least 64 rows per expert and the gate/up
+ * projection is not split. The results are the same bits either way. Same
+ * argument checks as moe_ffn_scratch_bytes.
+ */
+int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on);
+
+/*
  * moe_expert_ffn -- the grouped expert FFN over the expert-sorted rows
  * ([P3] s.1: gate/up projection, gated activation, weighted down projection
  * per job; [P1] s.1 finding 5 names the SwiGLU and down-projection epilogue

@@ -58,6 +58,7 @@ _SIGS = {
     "moe_ffn_scratch_bytes": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_ffn_splits": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int),
                        ctypes.POINTER(ctypes.c_int)],
+    "moe_ffn_big_cells": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int)],
     "moe_expert_ffn": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ, P],
     "moe_combine": [P, I64, P, I32, I32, I32, P, P],
     "moe_forward_workspace": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -141,6 +142,14 @@ def moe_ffn_splits(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int):
     _check("moe_ffn_splits",
            lib().moe_ffn_splits(E, d, f, tm, max_rows, dtype, ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def moe_ffn_big_cells(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int) -> bool:
+    """whether packed 16-bit gate/up runs its runs of 4 items on the 8-wavefront kernel"""
+    on = ctypes.c_int()
+    _check("moe_ffn_big_cells",
+           lib().moe_ffn_big_cells(E, d, f, tm, max_rows, dtype, ctypes.byref(on)))
+    return bool(on.value)
 
 
 def moe_forward_workspace(T, K, E, d, f, tm, dtype: int) -> int:

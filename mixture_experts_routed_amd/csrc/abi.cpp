@@ -60,7 +60,8 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
         !aligned(sw, 4) || !aligned(meta, 4) || !aligned(scratch, 16))
         return MOE_EINVAL;
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
-    if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max) return MOE_EINVAL;
+    if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max || z.blocks_big_gu > kI32Max)
+        return MOE_EINVAL;
     if (scratch_bytes < z.scratch_bytes) return MOE_EINVAL;
     return MOE_OK;
 }
@@ -332,6 +333,16 @@ int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
     *split_gateup = z.split_gu;
     *split_down = z.split_dn;
+    return MOE_OK;
+}
+
+int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on)
+{
+    if (!on || E < 1 || tm < 1 || max_rows < 1 || max_rows > kI32Max - 1024 || !dtype_ok(dtype) ||
+        d < 8 || f < 8 || d % 8 || f % 8)
+        return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    *on = moe::ffn_shape(E, tm, max_rows, d, f, dtype).big_gu ? 1 : 0;
     return MOE_OK;
 }
 

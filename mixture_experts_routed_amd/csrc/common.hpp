@@ -21,7 +21,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // The grouped FFN works on items of at most kItemRows rows of one expert; its
-// scratch holds an item count (first kCtlBytes) followed by the items.
+// scratch holds ctl (first kCtlBytes: ctl[0] = items, ctl[1] = items in runs
+// of 4) followed by the items.
 constexpr int kItemRows = 64;
 constexpr size_t kCtlBytes = 256;
 
@@ -36,7 +37,9 @@ struct WorkItem {
 };
 
 // Run of item q of an expert's n items: runs of 4 first, then one run of 2 if
-// at least 2 items remain, else single items.
+// at least 2 items remain, else single items. (Completing a last partial run
+// of 4 with empty items instead was measured slower on the long prompt in
+// chunks and no faster in one call.)
 __host__ __device__ inline int32_t item_run(int q, int n)
 {
     const int n4 = n & ~3;
@@ -44,6 +47,17 @@ __host__ __device__ inline int32_t item_run(int q, int n)
     const int q2 = q - n4;
     if (n - n4 >= 2 && q2 < 2) return 2 | (q2 << 8);
     return 1;
+}
+
+// Position of item q of an expert's n items in the work list. The items in
+// runs of 4 of every expert come first, in ascending expert order, then the
+// remaining items (runs of 2 and single items), also by expert. qbefore and
+// rbefore count the items of lower experts in each part; quad_items is the
+// number of items in runs of 4 over all experts.
+__host__ __device__ inline int item_slot(int q, int n, int qbefore, int rbefore, int quad_items)
+{
+    const int n4 = n & ~3;
+    return q < n4 ? qbefore + q : quad_items + rbefore + (q - n4);
 }
 
 __device__ __forceinline__ int wave_sum(int v)

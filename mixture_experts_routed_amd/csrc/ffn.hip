@@ -142,6 +142,9 @@ int64_t ffn_max_items(int E, int tm, int64_t max_rows)
     return max_rows / kItemRows + 1 + (E < per_tile ? E : per_tile);
 }
 
+// A run of 4 items spans more than 3 * 64 rows of one expert.
+int64_t ffn_max_quads(int64_t max_rows) { return max_rows / (3 * kItemRows + 1); }
+
 // ---- host-side shape of the two grouped GEMMs ------------------------------
 namespace {
 
@@ -151,6 +154,9 @@ int group_cols(bool gateup) { return kWavesPerBlock * (gateup ? 16 * kNpl : 32 *
 // Split-K is used when fewer than this many (item, column group) cells exist
 // at most: about two workgroups per CU.
 constexpr int64_t kTargetCells = 512;
+// The 8-wavefront kernel takes the runs of 4 items when the plan bound allows
+// this many rows per expert on average.
+constexpr int64_t kBigMinRowsPerExpert = 64;
 constexpr int kMinStepsPerSplit = 8;
 constexpr int kMaxSplit = 8;
 
@@ -183,6 +189,8 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
     split_for(z.max_items * gs_dn, f, kstep, &z.split_dn, &z.steps_dn);
     z.blocks_gu = (z.max_items * gs_gu * z.split_gu + 7) / 8 * 8;
     z.blocks_dn = (z.max_items * gs_dn * z.split_dn + 7) / 8 * 8;
+    z.big_gu = dtype != 0 && z.split_gu == 1 && max_rows >= kBigMinRowsPerExpert * (int64_t)E;
+    z.blocks_big_gu = (ffn_max_quads(max_rows) * ((f + 127) / 128) + 7) / 8 * 8;
     z.plane_gu = max_rows * 2 * (int64_t)f;
     z.plane_dn = max_rows * (int64_t)d;
     const size_t pg = z.split_gu > 1 ? (size_t)z.split_gu * z.plane_gu * 4 : 0;
@@ -193,13 +201,13 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
 }
 
 // Work list: each expert's row range [eoff[e], eoff[e+1]) cut into items of at
-// most kItemRows rows, in ascending expert order. Ranges are clamped to
-// [0, max_rows] so that made-up offsets cannot lead outside the buffers.
+// most kItemRows rows; runs of 4 items first (item_slot). Ranges are clamped
+// to [0, max_rows] so that made-up offsets cannot lead outside the buffers.
 __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ eoff, int E,
                                                    int64_t max_rows, int32_t *__restrict__ ctl,
                                                    WorkItem *__restrict__ items, int max_items)
 {
-    __shared__ int s_sum[16];
+    __shared__ int s_q[16], s_r[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int r0 = 0, rows = 0;
     if (tid < E) {
@@ -210,19 +218,24 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
         rows = (int)(b - a);
     }
     const int n = (rows + kItemRows - 1) / kItemRows;
-    const int incl = wave_inclusive_scan(n, lane);
-    if (lane == 63) s_sum[wv] = incl;
+    const int n4 = n & ~3;
+    const int qincl = wave_inclusive_scan(n4, lane);
+    const int rincl = wave_inclusive_scan(n - n4, lane);
+    if (lane == 63) {
+        s_q[wv] = qincl;
+        s_r[wv] = rincl;
+    }
     __syncthreads();
-    int before = 0, total = 0;
+    int qbefore = qincl - n4, rbefore = rincl - (n - n4), qtotal = 0, rtotal = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int v = s_sum[q];
-        before += (q < wv) ? v : 0;
-        total += v;
+        qbefore += (q < wv) ? s_q[q] : 0;
+        rbefore += (q < wv) ? s_r[q] : 0;
+        qtotal += s_q[q];
+        rtotal += s_r[q];
     }
-    const int start = before + incl - n;
     for (int q = 0; q < n; ++q) {
-        const int idx = start + q;
+        const int idx = item_slot(q, n, qbefore, rbefore, qtotal);
         if (idx < max_items) {
             WorkItem it;
             it.expert = tid;
@@ -232,7 +245,10 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
             items[idx] = it;
         }
     }
-    if (tid == 0) ctl[0] = min(total, max_items);
+    if (tid == 0) {
+        ctl[0] = min(qtotal + rtotal, max_items);
+        ctl[1] = min(qtotal, max_items) & ~3;
+    }
 }
 
 // ---- raw buffer loads -----------------------------------------------------
@@ -388,6 +404,7 @@ struct GemmArgs {
     int Kd, N;
     int nsplit;       // K splits per (item, column group)
     int split_steps;  // K-steps per split
+    int skip_quads;   // 1: the items in runs of 4 (the first ctl[1]) are left to k_gateup_big
 };
 
 // Epilogue of one wavefront: acc[m][mt][c][r] is the output at row
@@ -887,10 +904,12 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     const int gs = (p.N + 4 * SW - 1) / (4 * SW);       // column groups per item
     const int per_item = gs * p.nsplit;
     const int nitems = ctl[0];
-    const int lb = xcd_logical_block(nitems * per_item);
+    const int ifirst = p.skip_quads ? min(ctl[1], nitems) : 0;
+    const int lb = xcd_logical_block((nitems - ifirst) * per_item);
     if (lb < 0) return;  // whole workgroup: no barrier reached
-    const int i = lb / per_item;
-    const int rem = lb - i * per_item;
+    const int il = lb / per_item;  // item ifirst + il
+    const int i = ifirst + il;
+    const int rem = lb - il * per_item;
     const int g = rem / p.nsplit, split = rem - g * p.nsplit;
     const int kb = split * p.split_steps * KSTEP;
     const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
@@ -915,6 +934,162 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     case 3: wide_cells<T, GATEUP, GATHERED, PACKED, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
     default: wide_cells<T, GATEUP, GATHERED, PACKED, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
     }
+}
+
+// ---- big cells: runs of 4 items on 8 wavefronts (gate/up, packed, 16-bit) ---
+// An expert with hundreds of rows (a long prompt in one call) turns the
+// gate/up projection from weight streaming into a dense GEMM bound by the
+// matrix cores; the 4-wavefront cells above then move too many operand bytes
+// per MFMA. A big cell is one run of 4 items (up to 256 rows) x 128 columns
+// of h (gate and up: 256 weight columns) on 512 threads, K-step 64:
+//  * both operands go through LDS, double-buffered (2 x 64 KB): per step the
+//    256 rows x 128 bytes of A (each row one whole 128-byte line; a 16-byte
+//    chunk j of row r sits at chunk j ^ (r & 7), so the MFMA-order reads and
+//    the row-order writes are both free of bank conflicts) and the 4 packed
+//    4 KB tiles of each weight matrix (already in MFMA lane order);
+//  * wavefront (wr, wc) computes rows 64*wr.. of the run and the 64 columns
+//    of packed slice 2*(cb & 1) + wc: the same 2 x 4 x 4 accumulators, MFMA
+//    sequence and epilogue as a tall cell, so the results are the same bits;
+//  * global loads run two steps ahead in two register stages; the stage of
+//    step s+1 is written to the other LDS buffer halfway through the MFMAs
+//    of step s (one barrier per step).
+constexpr int kBigThreads = 512;
+constexpr int kBigCols = 128;                     // h columns per workgroup
+constexpr int kBigAU4 = 4 * kItemRows * 8;        // A tile: 256 rows x 8 chunks
+constexpr int kBigBU4 = 2 * 2 * 512;              // B tile: 2 sub-steps x 2 matrices x 8 KB
+constexpr int kBigBufU4 = kBigAU4 + kBigBU4;      // one buffer: 64 KB
+
+template <typename T, bool GATHERED>
+__global__ __launch_bounds__(kBigThreads) void k_gateup_big(const GemmArgs p,
+                                                             const int32_t *__restrict__ ctl,
+                                                             const WorkItem *__restrict__ items)
+{
+    static_assert(sizeof(T) == 2, "big cells: 16-bit element types");
+    constexpr int ES = 2;
+    __shared__ uint4 lds[2 * kBigBufU4];
+    const int Kd = p.Kd, N = p.N;
+    const int ncb = (N + kBigCols - 1) / kBigCols;
+    const int nquads = min(ctl[1], ctl[0]) / 4;
+    const int lb = xcd_logical_block(nquads * ncb);
+    if (lb < 0) return;  // whole workgroup: no barrier reached
+    const int qd = lb / ncb, cb = lb - qd * ncb;
+    const WorkItem first = items[4 * qd];
+    const WorkItem last = items[4 * qd + 3];
+    const int expert = first.expert, row0 = first.row0;
+    const int nvalid = max(0, min(4 * kItemRows, last.row0 + last.nrows - row0));
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave & 3, wc = wave >> 2;
+    const int nq = lane & 15, kg = lane >> 4;
+
+    // B: packed tiles (expert, column group cb/2, step s, slices w0, w0+1)
+    const PackedGeom z = packed_geom(Kd, N, true, ES);
+    const int w0 = 2 * (cb & 1);
+    const size_t gbase = ((size_t)expert * z.gs + (cb >> 1)) * z.nst * z.step_bytes;
+    const uint32_t grange = (uint32_t)z.nst * z.step_bytes;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(static_cast<const char *>(p.B1) + gbase, grange);
+    const uint32_t vb = (uint32_t)w0 * 4096u + (uint32_t)tid * 16u;
+
+    // A: this thread's 16-byte chunk ch of rows rr + 64*i of the run
+    const int ch = tid & 7, rr = tid >> 3;
+    __amdgpu_buffer_rsrc_t ra;
+    uint32_t va[4];
+    if constexpr (GATHERED) {
+        ra = make_rsrc(p.A, (uint32_t)((size_t)p.a_rows * Kd * ES));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rr + 64 * i;
+            const int t = r < nvalid ? p.stok[row0 + r] : -1;
+            va[i] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
+        }
+    } else {
+        ra = make_rsrc(static_cast<const T *>(p.A) + (size_t)row0 * Kd,
+                       (uint32_t)((size_t)nvalid * Kd * ES));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(rr + 64 * i) * (uint32_t)Kd * ES;
+    }
+    const int aslot = rr * 8 + (ch ^ (rr & 7));  // + 512 * i for row rr + 64 * i
+
+    float4_t acc[2][kMT][kNpl];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int c = 0; c < kNpl; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Stage {
+        uint4 a[4];
+        uint4 b[4];  // [sub-step][matrix]
+    };
+    auto load = [&](Stage &st, int step) {
+        // chunks past Kd (the next row's data) are read at an offset past the
+        // descriptor's range instead, which returns zeros: no masking of the
+        // loaded data, so no wait for it before it is written to LDS
+        const int ka = 64 * step + 8 * ch;
+        const bool kin = ka < Kd;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.a[i] = Ld<16>::run(ra, kin ? va[i] + (uint32_t)ka * ES : 0x80000000u, 0u);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            const uint32_t o = vb + (uint32_t)(2 * step + ss) * z.step_bytes;
+            st.b[2 * ss] = Ld<16, kNT>::run(rg, o, 0u);
+            st.b[2 * ss + 1] = Ld<16, kNT>::run(ru, o, 0u);
+        }
+    };
+    auto store = [&](const Stage &st, uint4 *buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf[aslot + 512 * i] = st.a[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf[kBigAU4 + 512 * j + tid] = st.b[j];
+    };
+    const int nsteps = (Kd + 63) / 64;
+    // the MFMAs of half ss (32 K) of a step
+    auto compute = [&](const uint4 *buf, int step, int ss) {
+        if (2 * step + ss >= z.nst) return;  // K tail: the tall cells run no such step
+        uint4 a[kMT];
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+            const int row = 64 * wr + 16 * mt + nq;
+            a[mt] = buf[row * 8 + ((4 * ss + kg) ^ (nq & 7))];
+        }
+#pragma unroll
+        for (int c = 0; c < kNpl; ++c)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const uint4 b = buf[kBigAU4 + 512 * (2 * ss + m) + 256 * wc + 64 * c + lane];
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt)
+                    acc[m][mt][c] = Elt<T>::mfma(a[mt], b, acc[m][mt][c]);
+            }
+    };
+    // One step: loads of step + 2 into the free register stage, the MFMAs of
+    // this step from LDS, and, between its two halves, the stage holding step + 1
+    // written to the other LDS buffer (read by no wavefront since the last
+    // barrier). Loads past the end read zeros (range-checked) and are never used.
+    auto iter = [&](Stage &fr, const Stage &nx, int step) {
+        load(fr, step + 2);
+        const uint4 *buf = lds + (step & 1) * kBigBufU4;
+        compute(buf, step, 0);
+        store(nx, lds + ((step + 1) & 1) * kBigBufU4);
+        compute(buf, step, 1);
+        __syncthreads();
+    };
+
+    Stage s0, s1;
+    load(s0, 0);
+    load(s1, 1);
+    store(s0, lds);
+    __syncthreads();
+    for (int step = 0; step < nsteps; step += 2) {
+        iter(s0, s1, step);
+        if (step + 1 < nsteps) iter(s1, s0, step + 1);
+    }
+    const WorkItem it = items[4 * qd + wr];
+    store_cells<T, true, kMT>(p, it, kBigCols * cb + 64 * wc + kNpl * nq, kg, acc, nullptr, 0);
 }
 
 // ---- split-K reductions (fixed split order) --------------------------------
@@ -1028,6 +1203,18 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     p.Kd = d;
     p.N = f;
     const dim3 grid((unsigned)z.blocks_gu);
+    if constexpr (PACKED && sizeof(T) == 2) {
+        if (z.big_gu && z.blocks_big_gu > 0) {
+            p.skip_quads = 1;
+            const dim3 bgrid((unsigned)z.blocks_big_gu);
+            if (gathered)
+                hipLaunchKernelGGL((k_gateup_big<T, true>), bgrid, dim3(kBigThreads), 0, s, p,
+                                   ctl_of(scratch), items_of(scratch));
+            else
+                hipLaunchKernelGGL((k_gateup_big<T, false>), bgrid, dim3(kBigThreads), 0, s, p,
+                                   ctl_of(scratch), items_of(scratch));
+        }
+    }
     if (gathered)  // rows gathered from x through stok
         hipLaunchKernelGGL((k_expert_gemm<T, true, true, PACKED>), grid, dim3(256), 0, s, p,
                            ctl_of(scratch), items_of(scratch));

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
 {
     __shared__ int s_tot[kMaxExperts], s_before[kMaxExperts], s_eoff[kMaxExperts];
     __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
-    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_isum[16];
+    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x;
     for (int e = tid; e < E; e += kPlanBlock) {
@@ -256,12 +256,15 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int mx = wave_max(c);
     skip = wave_sum(skip);
     bad = wave_sum(bad);
-    // work items of this expert (only needed by workgroup 0)
+    // work items of this expert, in runs of 4 and not (only needed by workgroup 0)
     const int nit = (rows + kItemRows - 1) / kItemRows;
-    const int iincl = wave_inclusive_scan(nit, lane);
+    const int nit4 = nit & ~3;
+    const int qincl = wave_inclusive_scan(nit4, lane);
+    const int rincl = wave_inclusive_scan(nit - nit4, lane);
     if (lane == 63) {
         s_sum[wv] = incl;
-        s_isum[wv] = iincl;
+        s_qsum[wv] = qincl;
+        s_rsum[wv] = rincl;
     }
     if (lane == 0) {
         s_act[wv] = act;
@@ -270,14 +273,17 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         s_bad[wv] = bad;
     }
     __syncthreads();
-    int before = 0, total = 0, ibefore = 0, itotal = 0;
+    int before = 0, total = 0, qbefore = qincl - nit4, rbefore = rincl - (nit - nit4);
+    int qtotal = 0, rtotal = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int v = s_sum[q], iv = s_isum[q];
+        const int v = s_sum[q];
         before += (q < wv) ? v : 0;
         total += v;
-        ibefore += (q < wv) ? iv : 0;
-        itotal += iv;
+        qbefore += (q < wv) ? s_qsum[q] : 0;
+        rbefore += (q < wv) ? s_rsum[q] : 0;
+        qtotal += s_qsum[q];
+        rtotal += s_rsum[q];
     }
     const int start = before + incl - rows;
     if (tid < E) {
@@ -294,9 +300,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             }
             for (int j = start / tm; j < (start + rows) / tm; ++j) tiles[j] = tid;
             if (items) {
-                const int istart = ibefore + iincl - nit;
                 for (int q = 0; q < nit; ++q) {
-                    const int idx = istart + q;
+                    const int idx = item_slot(q, nit, qbefore, rbefore, qtotal);
                     const int r0 = start + q * kItemRows;
                     if (idx < max_items && r0 < max_rows) {
                         WorkItem it;
@@ -330,7 +335,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             meta[kMetaTm] = tm;
             meta[kMetaE] = E;
             meta[kMetaK] = K;
-            if (items) ctl[0] = min(itotal, max_items);
+            if (items) {
+                ctl[0] = min(qtotal + rtotal, max_items);
+                ctl[1] = min(qtotal, max_items) & ~3;
+            }
         }
     }
 

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (POLLUTE, TOL, abi, custom, dev, host, make_case, polluted, rel_err, say,
-                      synth)
+from gpu_util import (POLLUTE, TOL, TORCH16, abi, custom, dev, host, make_case, polluted,
+                      rel_err, say, synth)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,7 @@ def test_ffn_configs_sampled(name):
     g = np.random.default_rng(cfg.seed)
     n = min(len(valid), 96)
     ent = np.unique(np.concatenate([valid[:4], valid[-4:], g.choice(valid, n, replace=False)]))
-    if name == "long_skewed_fp16":  # include entries of the heaviest expert (several work items)
+    if cfg.bias == "zipf1.1":  # include entries of the heaviest expert (several work items)
         top = np.bincount(flat[valid], minlength=cfg.E).argmax()
         heavy = valid[flat[valid] == top]
         ent = np.unique(np.concatenate([ent, heavy[:: max(1, len(heavy) // 24)]]))
@@ -132,3 +132,73 @@ def test_ffn_launch_paths(cfg, sgu, sdn, tall):
     assert (runs[4] + runs[2] > 0) == tall, runs
     say(f"[ffn paths] {cfg.name}: splits={splits} runs={runs}")
     run_ffn(case, case.ids, case.w, case.x)
+
+
+def worklist_model(eoff, E, max_rows):
+    """The grouped FFN's work list as the header describes it: each expert's
+    rows cut into items of 64; per expert runs of 4 items first, then a run of
+    2 if at least 2 items remain, then single items; the items in runs of 4 of
+    all experts come first (ascending expert), then the others (ascending
+    expert); run = length | index << 8. Returns (items [n, 4], items in runs of
+    4)."""
+    quad, rest = [], []
+    for e in range(E):
+        a = min(max(int(eoff[e]), 0), max_rows)
+        b = min(max(int(eoff[e + 1]), a), max_rows)
+        n = (b - a + 63) // 64
+        n4 = n & ~3
+        for q in range(n):
+            if q < n4:
+                run = 4 | ((q & 3) << 8)
+            elif n - n4 >= 2 and q - n4 < 2:
+                run = 2 | ((q - n4) << 8)
+            else:
+                run = 1
+            (quad if q < n4 else rest).append((e, a + 64 * q, min(64, b - a - 64 * q), run))
+    return np.array(quad + rest, np.int32).reshape(-1, 4), len(quad)
+
+
+WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3, f=64,
+                                            dtype="f16", bias="zipf1.1")]
+
+
+@pytest.mark.parametrize("cfg", WL, ids=[c.name for c in WL])
+@pytest.mark.parametrize("fused", [False, True], ids=["moe_expert_ffn", "moe_forward"])
+def test_worklist_layout(cfg, fused):
+    """the work list the FFN kernels consume (written by the worklist kernel
+    for moe_expert_ffn, by the one-launch plan for moe_forward) equals the
+    model above"""
+    ids, w = synth.routing(cfg)
+    T, K = ids.shape
+    p = oracle.plan(ids, w, cfg.E, cfg.tm)
+    z = abi.moe_plan_sizes(T, K, cfg.E, cfg.tm)
+    R = z.max_rows
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    want, nfour = worklist_model(p["eoff"], cfg.E, R)
+    say(f"[worklist] {cfg.name} {'forward' if fused else 'expert_ffn'}")
+    if fused:
+        x = torch.zeros((T, cfg.d), dtype=TORCH16[cfg.dtype], device="cuda")
+        wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
+               for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
+        _, ws = abi.forward(x, dev(ids), dev(w), *wts, tm=cfg.tm)
+        L = abi.moe_forward_layout(T, K, cfg.E, cfg.d, cfg.f, cfg.tm, dt)
+        scratch = ws[L.ffn_scratch:]
+    else:
+        nr = len(p["stok"])
+        stok = np.full(R, -1, np.int32)
+        stok[:nr] = p["stok"]
+        sw = np.zeros(R, np.float32)
+        sw[:nr] = p["sw"]
+        scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt),
+                              dtype=torch.uint8, device="cuda")
+        xs = torch.zeros((R, cfg.d), dtype=TORCH16[cfg.dtype], device="cuda")
+        h = torch.empty((R, cfg.f), dtype=TORCH16[cfg.dtype], device="cuda")
+        y = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
+        wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
+               for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
+        abi.moe_expert_ffn(xs, *wts, dt, cfg.E, cfg.d, cfg.f, cfg.tm, dev(p["eoff"]), dev(stok),
+                           dev(sw), dev(p["meta"]), R, h, y, scratch)
+    torch.cuda.synchronize()
+    raw = scratch[: 256 + 16 * len(want)].cpu().numpy().view(np.int32)
+    assert raw[0] == len(want) and raw[1] == nfour
+    assert np.array_equal(raw[64:].reshape(-1, 4), want)

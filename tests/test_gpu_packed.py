@@ -27,6 +27,21 @@ CASES = [
     custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
 ] + [c[0] for c in FFN_PATHS]
 
+# shapes whose packed 16-bit gate/up runs each expert's runs of 4 items on the
+# 8-wavefront kernel (plan bound >= 64 rows per expert, no K split): h columns
+# not a multiple of 128 (f = 320, 136), an odd number of 32-wide K-steps
+# (d = 328), a run whose last item is partial, tm = 1, runs followed by items
+# left to the 4-wavefront kernel, down projection split
+BIG = [
+    custom("big_cells_f16", T=2048, d=328, E=4, K=2, f=320, dtype="f16", bias="zipf1.1"),
+    custom("big_cells_bf16_tm1", T=1500, d=360, E=3, K=2, f=256, dtype="bf16", tm=1,
+           bias="zipf1.1", x_std=1.0),
+    custom("big_cells_f16_16e", T=4096, d=256, E=16, K=4, f=512, dtype="f16", bias="zipf1.1"),
+    custom("big_cells_bf16_24e", T=3000, d=264, E=24, K=3, f=136, dtype="bf16",
+           bias="normal0.5"),
+]
+CASES += BIG
+
 
 def packed_of(case):
     return abi.pack(case.d("wg"), case.d("wu"), case.d("wd"))
@@ -46,7 +61,30 @@ def test_forward_packed_equals_rowmajor(cfg):
     case.drop_device()
 
 
-@pytest.mark.parametrize("cfg", CASES[:5], ids=[c.name for c in CASES[:5]])
+@pytest.mark.parametrize("cfg", BIG, ids=[c.name for c in BIG])
+def test_big_cells_forward_vs_oracle(cfg):
+    """the packed layer on the shapes that take the 8-wavefront gate/up kernel,
+    every token against the oracle"""
+    z = abi.moe_plan_sizes(cfg.T, cfg.K, cfg.E, cfg.tm)
+    assert abi.moe_ffn_big_cells(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows,
+                                 abi.DTYPE_NAME[cfg.dtype])
+    case = make_case(cfg)
+    say(f"[packed forward, big cells] {cfg.name}")
+    x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
+    out, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                         packed=packed_of(case))
+    torch.cuda.synchronize()
+    got = host(out)
+    for round_h in (True, False):
+        ref = oracle.ffn(case.x, case.ids, case.w, case.wg, case.wu, case.wd, cfg.dtype, round_h)
+        assert rel_err(got, ref.astype(np.float32)) <= TOL[cfg.dtype], round_h
+    case.drop_device()
+
+
+FFN_CASES = CASES[:5] + BIG
+
+
+@pytest.mark.parametrize("cfg", FFN_CASES, ids=[c.name for c in FFN_CASES])
 def test_expert_ffn_packed_equals_rowmajor(cfg):
     case = make_case(cfg)
     T, K = case.ids.shape
@@ -82,7 +120,8 @@ def test_expert_ffn_packed_equals_rowmajor(cfg):
     case.drop_device()
 
 
-@pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16"])
+@pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16",
+                                  "long_onepass_fp16"])
 def test_forward_packed_full_size(name):
     """full-size workloads: packed == row-major bitwise, and packed vs the oracle
     on a sample of tokens"""
