@@ -188,14 +188,14 @@ int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int
                    int *split_down);
 
 /*
- * moe_ffn_big_cells -- host only: *on = 1 when, for these sizes, the packed
- * entry points (moe_expert_ffn_packed, moe_forward_packed) with fp16 or bf16
- * run each expert's runs of 4 work items (256 rows) of the gate/up projection
- * on 512-thread workgroups of 256 rows x 128 columns whose operands are staged
- * in LDS (a separate launch before the other work items), else 0. Used when
- * the plan bound averages at least 64 rows per expert and the gate/up
- * projection is not split. The results are the same bits either way. Same
- * argument checks as moe_ffn_scratch_bytes.
+ * moe_ffn_big_cells -- host only: which projections of the packed entry
+ * points (moe_expert_ffn_packed, moe_forward_packed) with fp16 or bf16 run
+ * each expert's runs of 4 work items (256 rows) on 512-thread workgroups of
+ * 256 rows x 256 weight columns whose operands are staged in LDS (a separate
+ * launch before the other work items): *on bit 0 = the gate/up projection,
+ * bit 1 = the down projection. Used when the plan bound averages at least 64
+ * rows per expert, for a projection that is not split. The results are the
+ * same bits either way. Same argument checks as moe_ffn_scratch_bytes.
  */
 int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on);
 

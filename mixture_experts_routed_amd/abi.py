@@ -144,12 +144,13 @@ def moe_ffn_splits(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int):
     return a.value, b.value
 
 
-def moe_ffn_big_cells(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int) -> bool:
-    """whether packed 16-bit gate/up runs its runs of 4 items on the 8-wavefront kernel"""
+def moe_ffn_big_cells(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int) -> int:
+    """which packed 16-bit projections run their runs of 4 items on the 8-wavefront
+    kernel: bit 0 gate/up, bit 1 down"""
     on = ctypes.c_int()
     _check("moe_ffn_big_cells",
            lib().moe_ffn_big_cells(E, d, f, tm, max_rows, dtype, ctypes.byref(on)))
-    return bool(on.value)
+    return on.value
 
 
 def moe_forward_workspace(T, K, E, d, f, tm, dtype: int) -> int:

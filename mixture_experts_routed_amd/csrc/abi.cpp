@@ -60,7 +60,8 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
         !aligned(sw, 4) || !aligned(meta, 4) || !aligned(scratch, 16))
         return MOE_EINVAL;
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
-    if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max || z.blocks_big_gu > kI32Max)
+    if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max || z.blocks_big_gu > kI32Max ||
+        z.blocks_big_dn > kI32Max)
         return MOE_EINVAL;
     if (scratch_bytes < z.scratch_bytes) return MOE_EINVAL;
     return MOE_OK;
@@ -342,7 +343,8 @@ int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, 
         d < 8 || f < 8 || d % 8 || f % 8)
         return MOE_EINVAL;
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
-    *on = moe::ffn_shape(E, tm, max_rows, d, f, dtype).big_gu ? 1 : 0;
+    const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
+    *on = (z.big_gu ? 1 : 0) | (z.big_dn ? 2 : 0);
     return MOE_OK;
 }
 

@@ -43,6 +43,9 @@ namespace moe {
 constexpr int kMT = kItemRows / 16;     // 16-row m-tiles per work item
 constexpr int kWavesPerBlock = 4;
 constexpr int kNpl = 4;                 // columns per lane and B stream
+// output columns per 8-wavefront big-cell workgroup: h columns (gate/up) or y
+// columns (down)
+constexpr int big_cols(bool gateup) { return gateup ? 128 : 256; }
 
 int ffn_rows_per_item() { return kItemRows; }
 
@@ -189,8 +192,11 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
     split_for(z.max_items * gs_dn, f, kstep, &z.split_dn, &z.steps_dn);
     z.blocks_gu = (z.max_items * gs_gu * z.split_gu + 7) / 8 * 8;
     z.blocks_dn = (z.max_items * gs_dn * z.split_dn + 7) / 8 * 8;
-    z.big_gu = dtype != 0 && z.split_gu == 1 && max_rows >= kBigMinRowsPerExpert * (int64_t)E;
-    z.blocks_big_gu = (ffn_max_quads(max_rows) * ((f + 127) / 128) + 7) / 8 * 8;
+    const bool big = dtype != 0 && max_rows >= kBigMinRowsPerExpert * (int64_t)E;
+    z.big_gu = big && z.split_gu == 1;
+    z.big_dn = big && z.split_dn == 1;
+    z.blocks_big_gu = (ffn_max_quads(max_rows) * ((f + big_cols(true) - 1) / big_cols(true)) + 7) / 8 * 8;
+    z.blocks_big_dn = (ffn_max_quads(max_rows) * ((d + big_cols(false) - 1) / big_cols(false)) + 7) / 8 * 8;
     z.plane_gu = max_rows * 2 * (int64_t)f;
     z.plane_dn = max_rows * (int64_t)d;
     const size_t pg = z.split_gu > 1 ? (size_t)z.split_gu * z.plane_gu * 4 : 0;
@@ -404,7 +410,7 @@ struct GemmArgs {
     int Kd, N;
     int nsplit;       // K splits per (item, column group)
     int split_steps;  // K-steps per split
-    int skip_quads;   // 1: the items in runs of 4 (the first ctl[1]) are left to k_gateup_big
+    int skip_quads;   // 1: the items in runs of 4 (the first ctl[1]) are left to k_big
 };
 
 // Epilogue of one wavefront: acc[m][mt][c][r] is the output at row
@@ -936,71 +942,106 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     }
 }
 
-// ---- big cells: runs of 4 items on 8 wavefronts (gate/up, packed, 16-bit) ---
-// An expert with hundreds of rows (a long prompt in one call) turns the
-// gate/up projection from weight streaming into a dense GEMM bound by the
-// matrix cores; the 4-wavefront cells above then move too many operand bytes
-// per MFMA. A big cell is one run of 4 items (up to 256 rows) x 128 columns
-// of h (gate and up: 256 weight columns) on 512 threads, K-step 64:
-//  * both operands go through LDS, double-buffered (2 x 64 KB): per step the
-//    256 rows x 128 bytes of A (each row one whole 128-byte line; a 16-byte
-//    chunk j of row r sits at chunk j ^ (r & 7), so the MFMA-order reads and
-//    the row-order writes are both free of bank conflicts) and the 4 packed
-//    4 KB tiles of each weight matrix (already in MFMA lane order);
-//  * wavefront (wr, wc) computes rows 64*wr.. of the run and the 64 columns
-//    of packed slice 2*(cb & 1) + wc: the same 2 x 4 x 4 accumulators, MFMA
-//    sequence and epilogue as a tall cell, so the results are the same bits;
-//  * global loads run two steps ahead in two register stages; the stage of
-//    step s+1 is written to the other LDS buffer halfway through the MFMAs
-//    of step s (one barrier per step).
+// ---- big cells: runs of 4 items on 8 wavefronts (packed, 16-bit) ------------
+// An expert with hundreds of rows (a long prompt in one call) turns its
+// projections from weight streaming into dense GEMMs bound by the matrix
+// cores; the 4-wavefront cells above then move too many operand bytes per
+// MFMA. A big cell is one run of 4 items (up to 256 rows) x 256 weight
+// columns (gate/up: 128 columns of h from each matrix; down: 256 columns of
+// y) on 512 threads, 64-wide K-steps:
+//  * a step's operands (A: 256 rows x 128 bytes; B: the 4 KB packed tiles of
+//    slices w0, w0+1 for two 32-wide MFMA steps, already in MFMA lane order)
+//    go straight from memory into one of 2 LDS buffers (buffer loads with
+//    the LDS flag, no registers), a step ahead of the MFMAs;
+//  * the MFMA operands of step s+1 are read from LDS into registers while the
+//    MFMAs of step s run, each into the register of the operand it replaces
+//    once that operand's last MFMA is issued; one barrier per step;
+//  * in LDS the 16-byte chunk j of A row r sits at chunk j ^ (r & 7): the
+//    MFMA-order reads are then free of bank conflicts;
+//  * wavefront (wr, wc) computes rows 64*wr.. of the run and packed slice
+//    w0 + wc: the same 2 x 4 x 4 accumulators, MFMA sequence and epilogue as
+//    a tall cell, so the results are the same bits.
+// The 2 buffers are separate LDS arrays and the step loop is unrolled by 2, so
+// that the compiler can tell a buffer's reads from the loads in flight into
+// the other and does not make the reads wait for those loads.
 constexpr int kBigThreads = 512;
-constexpr int kBigCols = 128;                     // h columns per workgroup
-constexpr int kBigAU4 = 4 * kItemRows * 8;        // A tile: 256 rows x 8 chunks
-constexpr int kBigBU4 = 2 * 2 * 512;              // B tile: 2 sub-steps x 2 matrices x 8 KB
-constexpr int kBigBufU4 = kBigAU4 + kBigBU4;      // one buffer: 64 KB
+constexpr int kBigAU4 = 4 * kItemRows * 8;    // A tile of one step: 256 rows x 8 chunks
+constexpr int kBigBufU4 = kBigAU4 + 4 * 512;  // + B: 2 halves x 16 KB = 64 KB
+// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum (no wait)
+constexpr int kWaitVm0 = 0x0F70;
 
-template <typename T, bool GATHERED>
-__global__ __launch_bounds__(kBigThreads) void k_gateup_big(const GemmArgs p,
-                                                             const int32_t *__restrict__ ctl,
-                                                             const WorkItem *__restrict__ items)
+template <typename T, bool GATEUP, bool GATHERED>
+__global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
+                                                      const int32_t *__restrict__ ctl,
+                                                      const WorkItem *__restrict__ items)
 {
     static_assert(sizeof(T) == 2, "big cells: 16-bit element types");
+    static_assert(GATEUP || !GATHERED, "the down projection reads h row-major");
     constexpr int ES = 2;
-    __shared__ uint4 lds[2 * kBigBufU4];
+    constexpr int BCOLS = big_cols(GATEUP);
+    __shared__ uint4 L0[kBigBufU4], L1[kBigBufU4];
+    __shared__ float2 rinfo[4 * kItemRows];
     const int Kd = p.Kd, N = p.N;
-    const int ncb = (N + kBigCols - 1) / kBigCols;
+    const int ncb = (N + BCOLS - 1) / BCOLS;
     const int nquads = min(ctl[1], ctl[0]) / 4;
     const int lb = xcd_logical_block(nquads * ncb);
     if (lb < 0) return;  // whole workgroup: no barrier reached
     const int qd = lb / ncb, cb = lb - qd * ncb;
     const WorkItem first = items[4 * qd];
     const WorkItem last = items[4 * qd + 3];
-    const int expert = first.expert, row0 = first.row0;
-    const int nvalid = max(0, min(4 * kItemRows, last.row0 + last.nrows - row0));
+    // workgroup-uniform by construction; said so, so that the buffer
+    // descriptors built from them stay in scalar registers
+    const int expert = __builtin_amdgcn_readfirstlane(first.expert);
+    const int row0 = __builtin_amdgcn_readfirstlane(first.row0);
+    const int nvalid = __builtin_amdgcn_readfirstlane(
+        max(0, min(4 * kItemRows, last.row0 + last.nrows - row0)));
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave & 3, wc = wave >> 2;
     const int nq = lane & 15, kg = lane >> 4;
+    const WorkItem it = items[4 * qd + wr];
+    float2 *my_rinfo = rinfo + kItemRows * wr;
+    if (!GATEUP && wc == 0) load_rinfo<true>(p, it, lane, my_rinfo);
 
-    // B: packed tiles (expert, column group cb/2, step s, slices w0, w0+1)
-    const PackedGeom z = packed_geom(Kd, N, true, ES);
+    // B: packed tiles (expert, column group cb/2, 32-wide K-step, slices w0,
+    // w0+1). Per half step: gate/up 2 x 8 KB (gate, then up: tiles w0, w0+1),
+    // down 16 KB (tiles (w0, 0), (w0, 1), (w0+1, 0), (w0+1, 1)). Wavefront w
+    // moves 4 KB of half w >> 2.
+    const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
     const int w0 = 2 * (cb & 1);
     const size_t gbase = ((size_t)expert * z.gs + (cb >> 1)) * z.nst * z.step_bytes;
     const uint32_t grange = (uint32_t)z.nst * z.step_bytes;
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
-    const __amdgpu_buffer_rsrc_t ru = make_rsrc(static_cast<const char *>(p.B1) + gbase, grange);
-    const uint32_t vb = (uint32_t)w0 * 4096u + (uint32_t)tid * 16u;
+    const int bhalf = wave >> 2;
+    __amdgpu_buffer_rsrc_t rb;
+    uint32_t vb;
+    if constexpr (GATEUP) {
+        rb = make_rsrc(static_cast<const char *>((wave >> 1) & 1 ? p.B1 : p.B0) + gbase, grange);
+        vb = (uint32_t)w0 * 4096u + (uint32_t)(wave & 1) * 4096u;
+    } else {
+        rb = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
+        vb = (uint32_t)w0 * 8192u + (uint32_t)(wave & 3) * 4096u;
+    }
+    vb += (uint32_t)lane * 16u;
+    const int bslot = kBigAU4 + 1024 * bhalf + 256 * (wave & 3);
+    // B operand (half h, matrix or slice half m, column quad c) of this wavefront
+    auto bidx = [&](int h, int m, int c) {
+        return kBigAU4 + 1024 * h + (GATEUP ? 512 * m + 256 * wc : 512 * wc + 256 * m) + 64 * c +
+               lane;
+    };
 
-    // A: this thread's 16-byte chunk ch of rows rr + 64*i of the run
-    const int ch = tid & 7, rr = tid >> 3;
+    // A: wavefront w moves rows 32 w .. 32 w + 31 of the run, 8 rows per
+    // instruction; lane l takes row 32 w + 8 i + (l >> 3) and fills its LDS
+    // chunk l & 7 with the row's K chunk (l & 7) ^ (l >> 3)
+    const int arow = 32 * wave + (lane >> 3);
+    const uint32_t achunk = (uint32_t)(8 * ((lane & 7) ^ (lane >> 3)));  // elements
     __amdgpu_buffer_rsrc_t ra;
     uint32_t va[4];
     if constexpr (GATHERED) {
         ra = make_rsrc(p.A, (uint32_t)((size_t)p.a_rows * Kd * ES));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = rr + 64 * i;
+            const int r = arow + 8 * i;
             const int t = r < nvalid ? p.stok[row0 + r] : -1;
             va[i] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
         }
@@ -1008,9 +1049,8 @@ __global__ __launch_bounds__(kBigThreads) void k_gateup_big(const GemmArgs p,
         ra = make_rsrc(static_cast<const T *>(p.A) + (size_t)row0 * Kd,
                        (uint32_t)((size_t)nvalid * Kd * ES));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(rr + 64 * i) * (uint32_t)Kd * ES;
+        for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(arow + 8 * i) * (uint32_t)Kd * ES;
     }
-    const int aslot = rr * 8 + (ch ^ (rr & 7));  // + 512 * i for row rr + 64 * i
 
     float4_t acc[2][kMT][kNpl];
 #pragma unroll
@@ -1020,76 +1060,90 @@ __global__ __launch_bounds__(kBigThreads) void k_gateup_big(const GemmArgs p,
 #pragma unroll
             for (int c = 0; c < kNpl; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    struct Stage {
-        uint4 a[4];
-        uint4 b[4];  // [sub-step][matrix]
-    };
-    auto load = [&](Stage &st, int step) {
-        // chunks past Kd (the next row's data) are read at an offset past the
-        // descriptor's range instead, which returns zeros: no masking of the
-        // loaded data, so no wait for it before it is written to LDS
-        const int ka = 64 * step + 8 * ch;
-        const bool kin = ka < Kd;
+    typedef __attribute__((address_space(3))) void *lds_ptr;
+    // the operands of step s into LDS buffer L; K chunks past Kd (the next
+    // row's data) and steps past the end are read at offsets past the
+    // descriptors' ranges, which return zeros
+    auto issue = [&](uint4 (&L)[kBigBufU4], int s) {
+        const uint32_t ka = (uint32_t)(64 * s) + achunk;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            st.a[i] = Ld<16>::run(ra, kin ? va[i] + (uint32_t)ka * ES : 0x80000000u, 0u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_ptr)(L + (32 * wave + 8 * i) * 8), 16,
+                (int)ka < Kd ? va[i] + ka * ES : 0x80000000u, 0, 0, 0);
+        const uint32_t o = vb + (uint32_t)(2 * s + bhalf) * z.step_bytes;
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-            const uint32_t o = vb + (uint32_t)(2 * step + ss) * z.step_bytes;
-            st.b[2 * ss] = Ld<16, kNT>::run(rg, o, 0u);
-            st.b[2 * ss + 1] = Ld<16, kNT>::run(ru, o, 0u);
-        }
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(L + bslot + 64 * j), 16,
+                                                     o + (uint32_t)j * 1024u, 0, 0, kNT);
     };
-    auto store = [&](const Stage &st, uint4 *buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) buf[aslot + 512 * i] = st.a[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) buf[kBigAU4 + 512 * j + tid] = st.b[j];
+    struct Frag {
+        uint4 a[2][kMT];
+        uint4 b[2][2][kNpl];
     };
-    const int nsteps = (Kd + 63) / 64;
-    // the MFMAs of half ss (32 K) of a step
-    auto compute = [&](const uint4 *buf, int step, int ss) {
-        if (2 * step + ss >= z.nst) return;  // K tail: the tall cells run no such step
-        uint4 a[kMT];
+    auto read_a = [&](Frag &f, const uint4 (&L)[kBigBufU4], int h) {
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             const int row = 64 * wr + 16 * mt + nq;
-            a[mt] = buf[row * 8 + ((4 * ss + kg) ^ (nq & 7))];
+            f.a[h][mt] = L[row * 8 + ((4 * h + kg) ^ (nq & 7))];
         }
-#pragma unroll
-        for (int c = 0; c < kNpl; ++c)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const uint4 b = buf[kBigAU4 + 512 * (2 * ss + m) + 256 * wc + 64 * c + lane];
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt)
-                    acc[m][mt][c] = Elt<T>::mfma(a[mt], b, acc[m][mt][c]);
-            }
     };
-    // One step: loads of step + 2 into the free register stage, the MFMAs of
-    // this step from LDS, and, between its two halves, the stage holding step + 1
-    // written to the other LDS buffer (read by no wavefront since the last
-    // barrier). Loads past the end read zeros (range-checked) and are never used.
-    auto iter = [&](Stage &fr, const Stage &nx, int step) {
-        load(fr, step + 2);
-        const uint4 *buf = lds + (step & 1) * kBigBufU4;
-        compute(buf, step, 0);
-        store(nx, lds + ((step + 1) & 1) * kBigBufU4);
-        compute(buf, step, 1);
+    auto read_b = [&](Frag &f, const uint4 (&L)[kBigBufU4], int h, int m, int c) {
+        f.b[h][m][c] = L[bidx(h, m, c)];
+    };
+    // Step s with operands f: the loads of step s+2 go to Lf (step s's buffer,
+    // whose reads were complete at the last barrier), step s+1's operands are
+    // read from Ln into f as their registers free up; then every read done
+    // and this wavefront's loads landed (the barrier's fence), barrier
+    const int nst = z.nst;  // 32-wide MFMA steps
+    const int nsteps = (nst + 1) / 2;
+    Frag f;
+    auto stepfn = [&](int s, const uint4 (&Ln)[kBigBufU4], uint4 (&Lf)[kBigBufU4]) {
+        issue(Lf, s + 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int c = 0; c < kNpl; ++c)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (2 * s + h < nst) {  // K tail: the tall cells run no such step
+#pragma unroll
+                        for (int mt = 0; mt < kMT; ++mt)
+                            acc[m][mt][c] = Elt<T>::mfma(f.a[h][mt], f.b[h][m][c], acc[m][mt][c]);
+                    }
+                    read_b(f, Ln, h, m, c);
+                    // keep this order: a read hoisted above the MFMAs would
+                    // hold a second set of operand registers
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            read_a(f, Ln, h);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
     };
 
-    Stage s0, s1;
-    load(s0, 0);
-    load(s1, 1);
-    store(s0, lds);
+    issue(L0, 0);
+    issue(L1, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-        iter(s0, s1, step);
-        if (step + 1 < nsteps) iter(s1, s0, step + 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        read_a(f, L0, h);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int c = 0; c < kNpl; ++c) read_b(f, L0, h, m, c);
     }
-    const WorkItem it = items[4 * qd + wr];
-    store_cells<T, true, kMT>(p, it, kBigCols * cb + 64 * wc + kNpl * nq, kg, acc, nullptr, 0);
+    __syncthreads();  // these reads done everywhere before step 2's loads reuse L0
+    // (no early exit from the unrolled loop: that made the compiler spill)
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        stepfn(s, L1, L0);
+        stepfn(s + 1, L0, L1);
+    }
+    if (s < nsteps) stepfn(s, L1, L0);
+    const int col = BCOLS * cb + (BCOLS / 2) * wc + kNpl * nq;
+    store_cells<T, GATEUP, kMT>(p, it, col, kg, acc, my_rinfo, 0);
 }
 
 // ---- split-K reductions (fixed split order) --------------------------------
@@ -1208,10 +1262,10 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
             p.skip_quads = 1;
             const dim3 bgrid((unsigned)z.blocks_big_gu);
             if (gathered)
-                hipLaunchKernelGGL((k_gateup_big<T, true>), bgrid, dim3(kBigThreads), 0, s, p,
+                hipLaunchKernelGGL((k_big<T, true, true>), bgrid, dim3(kBigThreads), 0, s, p,
                                    ctl_of(scratch), items_of(scratch));
             else
-                hipLaunchKernelGGL((k_gateup_big<T, false>), bgrid, dim3(kBigThreads), 0, s, p,
+                hipLaunchKernelGGL((k_big<T, true, false>), bgrid, dim3(kBigThreads), 0, s, p,
                                    ctl_of(scratch), items_of(scratch));
         }
     }
@@ -1241,6 +1295,13 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
     p.out = y;
     p.Kd = f;
     p.N = d;
+    if constexpr (PACKED && sizeof(T) == 2) {
+        if (z.big_dn && z.blocks_big_dn > 0) {
+            p.skip_quads = 1;
+            hipLaunchKernelGGL((k_big<T, false, false>), dim3((unsigned)z.blocks_big_dn),
+                               dim3(kBigThreads), 0, s, p, ctl_of(scratch), items_of(scratch));
+        }
+    }
     hipLaunchKernelGGL((k_expert_gemm<T, false, false, PACKED>), dim3((unsigned)z.blocks_dn),
                        dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch));
     if (z.split_dn > 1)

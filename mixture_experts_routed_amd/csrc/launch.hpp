@@ -49,10 +49,11 @@ struct FfnShape {
     int split_gu, steps_gu;  // gate/up: K splits and K-steps per split
     int split_dn, steps_dn;  // down
     int64_t blocks_gu, blocks_dn;  // workgroups per launch
-    // runs of 4 items of packed 16-bit gate/up on the 8-wavefront kernel (when
-    // not split): whether, and its grid (bound on runs x column blocks)
-    bool big_gu;
-    int64_t blocks_big_gu;
+    // runs of 4 items of the packed 16-bit projections on the 8-wavefront
+    // kernel (when not split): whether, and its grids (bound on runs x column
+    // blocks)
+    bool big_gu, big_dn;
+    int64_t blocks_big_gu, blocks_big_dn;
     int64_t plane_gu, plane_dn;    // floats per partial plane
     size_t part_offset;            // byte offset of the partial planes
     size_t scratch_bytes;

@@ -63,13 +63,15 @@ def test_forward_packed_equals_rowmajor(cfg):
 
 @pytest.mark.parametrize("cfg", BIG, ids=[c.name for c in BIG])
 def test_big_cells_forward_vs_oracle(cfg):
-    """the packed layer on the shapes that take the 8-wavefront gate/up kernel,
-    every token against the oracle"""
+    """the packed layer on the shapes that take the 8-wavefront kernels (gate/up
+    always, down unless it is split), every token against the oracle"""
     z = abi.moe_plan_sizes(cfg.T, cfg.K, cfg.E, cfg.tm)
-    assert abi.moe_ffn_big_cells(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows,
-                                 abi.DTYPE_NAME[cfg.dtype])
+    big = abi.moe_ffn_big_cells(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows, abi.DTYPE_NAME[cfg.dtype])
+    splits = abi.moe_ffn_splits(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows, abi.DTYPE_NAME[cfg.dtype])
+    assert big & 1  # gate/up
+    assert bool(big & 2) == (splits[1] == 1)  # down, unless split along f
     case = make_case(cfg)
-    say(f"[packed forward, big cells] {cfg.name}")
+    say(f"[packed forward, big cells {big}] {cfg.name}")
     x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
     out, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
                          packed=packed_of(case))
