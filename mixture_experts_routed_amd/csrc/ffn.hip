@@ -350,7 +350,13 @@ template <> struct Elt<float> {
     static constexpr int KR = 4;
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) in
+// place of an IEEE division: an order of magnitude below the error of the
+// fp16/bf16 SwiGLU output it feeds, and a fraction of the epilogue's time
+__device__ __forceinline__ float silu(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // 16-bit B operand: RP consecutive K-rows of 4 columns each (row i = K-value
 // i). Column c of them as RP/2 words of an MFMA operand (element i = K-row i).
@@ -416,7 +422,7 @@ struct GemmArgs {
 // Epilogue of one wavefront: acc[m][mt][c][r] is the output at row
 // 16*mt + 4*kg + r of item `it` and column col + c (+ HALF for m = 1 of the
 // down projection). rinfo[l] = (router weight, token) of the item's row l.
-template <typename T, bool GATEUP, int NMT>
+template <typename T, bool GATEUP, int NMT, bool MAY_SPLIT = true>
 __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &it, int col, int kg,
                                             const float4_t (&acc)[2][NMT][kNpl],
                                             const float2 *__restrict__ rinfo, int split)
@@ -425,7 +431,7 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
     constexpr int HALF = GATEUP ? 0 : 16 * kNpl;
     const int N = p.N;
     if (col >= N) return;
-    const bool partial = p.nsplit > 1;
+    const bool partial = MAY_SPLIT && p.nsplit > 1;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -948,27 +954,36 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
 // cores; the 4-wavefront cells above then move too many operand bytes per
 // MFMA. A big cell is one run of 4 items (up to 256 rows) x 256 weight
 // columns (gate/up: 128 columns of h from each matrix; down: 256 columns of
-// y) on 512 threads, 64-wide K-steps:
-//  * a step's operands (A: 256 rows x 128 bytes; B: the 4 KB packed tiles of
-//    slices w0, w0+1 for two 32-wide MFMA steps, already in MFMA lane order)
-//    go straight from memory into one of 2 LDS buffers (buffer loads with
-//    the LDS flag, no registers), a step ahead of the MFMAs;
+// y) on 512 threads, in 32-wide K-steps:
+//  * a step's operands (A: 256 rows x 64 bytes; B: the 4 KB packed tiles of
+//    slices w0, w0+1, already in MFMA lane order) go straight from memory into
+//    one of NB LDS buffers of 32 KB (buffer loads with the LDS flag, no
+//    registers), NB - 1 steps ahead of the MFMAs, and are waited for 2 steps
+//    (gate/up, NB = 5: the whole LDS) or 1 step (down, NB = 4, plus the rows'
+//    router weights) before use: these loads spend about as long in the memory
+//    system as a step's MFMAs take;
+//  * the loads keep the default cache policy: the operands of a step are read
+//    by several workgroups at about the same time (the rows by every column
+//    block of the run, the weights by the runs of the same expert), which then
+//    hit in L2 (non-temporal weight loads were measured 10% slower);
 //  * the MFMA operands of step s+1 are read from LDS into registers while the
 //    MFMAs of step s run, each into the register of the operand it replaces
-//    once that operand's last MFMA is issued; one barrier per step;
-//  * in LDS the 16-byte chunk j of A row r sits at chunk j ^ (r & 7): the
-//    MFMA-order reads are then free of bank conflicts;
+//    once that operand's last MFMA is issued; one barrier per step, as inline
+//    asm with a memory clobber (__syncthreads()'s release fence would wait for
+//    every load in flight);
+//  * in LDS the 16-byte chunk j of A row r sits at chunk j ^ ((r >> 1) & 3):
+//    the MFMA-order reads are then free of bank conflicts;
 //  * wavefront (wr, wc) computes rows 64*wr.. of the run and packed slice
 //    w0 + wc: the same 2 x 4 x 4 accumulators, MFMA sequence and epilogue as
 //    a tall cell, so the results are the same bits.
-// The 2 buffers are separate LDS arrays and the step loop is unrolled by 2, so
+// The buffers are separate LDS arrays and the step loop is unrolled by NB, so
 // that the compiler can tell a buffer's reads from the loads in flight into
-// the other and does not make the reads wait for those loads.
+// the others and does not make the reads wait for those loads.
 constexpr int kBigThreads = 512;
-constexpr int kBigAU4 = 4 * kItemRows * 8;    // A tile of one step: 256 rows x 8 chunks
-constexpr int kBigBufU4 = kBigAU4 + 4 * 512;  // + B: 2 halves x 16 KB = 64 KB
-// s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maximum (no wait)
-constexpr int kWaitVm0 = 0x0F70;
+constexpr int kDeepAU4 = 4 * kItemRows * 4;   // A tile of one step: 256 rows x 4 chunks
+constexpr int kDeepBufU4 = kDeepAU4 + 1024;   // + B: 16 KB = 32 KB per buffer
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maximum (no wait)
+constexpr int wait_vm(int n) { return 0x0F70 | n; }
 
 template <typename T, bool GATEUP, bool GATHERED>
 __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
@@ -979,8 +994,11 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     static_assert(GATEUP || !GATHERED, "the down projection reads h row-major");
     constexpr int ES = 2;
     constexpr int BCOLS = big_cols(GATEUP);
-    __shared__ uint4 L0[kBigBufU4], L1[kBigBufU4];
-    __shared__ float2 rinfo[4 * kItemRows];
+    constexpr int NB = GATEUP ? 5 : 4;        // LDS buffers
+    constexpr int VM = 4 * (NB - 3);          // loads of this wavefront still in flight
+    __shared__ uint4 L0[kDeepBufU4], L1[kDeepBufU4], L2[kDeepBufU4], L3[kDeepBufU4],
+        L4[GATEUP ? kDeepBufU4 : 1];
+    __shared__ float2 rinfo[GATEUP ? 1 : 4 * kItemRows];
     const int Kd = p.Kd, N = p.N;
     const int ncb = (N + BCOLS - 1) / BCOLS;
     const int nquads = min(ctl[1], ctl[0]) / 4;
@@ -1001,47 +1019,40 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     const int wr = wave & 3, wc = wave >> 2;
     const int nq = lane & 15, kg = lane >> 4;
     const WorkItem it = items[4 * qd + wr];
-    float2 *my_rinfo = rinfo + kItemRows * wr;
+    float2 *my_rinfo = GATEUP ? nullptr : rinfo + kItemRows * wr;
     if (!GATEUP && wc == 0) load_rinfo<true>(p, it, lane, my_rinfo);
 
-    // B: packed tiles (expert, column group cb/2, 32-wide K-step, slices w0,
-    // w0+1). Per half step: gate/up 2 x 8 KB (gate, then up: tiles w0, w0+1),
-    // down 16 KB (tiles (w0, 0), (w0, 1), (w0+1, 0), (w0+1, 1)). Wavefront w
-    // moves 4 KB of half w >> 2.
+    // B: per step the packed tiles of slices w0, w0+1: gate/up 8 KB of gate,
+    // then 8 KB of up; down 16 KB (tiles (w0, 0), (w0, 1), (w0+1, 0),
+    // (w0+1, 1)). Wavefront w moves KB 2 w and 2 w + 1 of these 16.
     const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
     const int w0 = 2 * (cb & 1);
     const size_t gbase = ((size_t)expert * z.gs + (cb >> 1)) * z.nst * z.step_bytes;
     const uint32_t grange = (uint32_t)z.nst * z.step_bytes;
-    const int bhalf = wave >> 2;
     __amdgpu_buffer_rsrc_t rb;
     uint32_t vb;
     if constexpr (GATEUP) {
-        rb = make_rsrc(static_cast<const char *>((wave >> 1) & 1 ? p.B1 : p.B0) + gbase, grange);
-        vb = (uint32_t)w0 * 4096u + (uint32_t)(wave & 1) * 4096u;
+        rb = make_rsrc(static_cast<const char *>(wave >> 2 ? p.B1 : p.B0) + gbase, grange);
+        vb = (uint32_t)w0 * 4096u + (uint32_t)(wave & 3) * 2048u;
     } else {
         rb = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
-        vb = (uint32_t)w0 * 8192u + (uint32_t)(wave & 3) * 4096u;
+        vb = (uint32_t)w0 * 8192u + (uint32_t)wave * 2048u;
     }
     vb += (uint32_t)lane * 16u;
-    const int bslot = kBigAU4 + 1024 * bhalf + 256 * (wave & 3);
-    // B operand (half h, matrix or slice half m, column quad c) of this wavefront
-    auto bidx = [&](int h, int m, int c) {
-        return kBigAU4 + 1024 * h + (GATEUP ? 512 * m + 256 * wc : 512 * wc + 256 * m) + 64 * c +
-               lane;
-    };
+    const int bslot = kDeepAU4 + 128 * wave;
 
-    // A: wavefront w moves rows 32 w .. 32 w + 31 of the run, 8 rows per
-    // instruction; lane l takes row 32 w + 8 i + (l >> 3) and fills its LDS
-    // chunk l & 7 with the row's K chunk (l & 7) ^ (l >> 3)
-    const int arow = 32 * wave + (lane >> 3);
-    const uint32_t achunk = (uint32_t)(8 * ((lane & 7) ^ (lane >> 3)));  // elements
+    // A: wavefront w moves rows 32 w .. 32 w + 31, 16 rows per instruction;
+    // lane l takes row 32 w + 16 i + (l >> 2) and fills its LDS chunk l & 3
+    // with the row's K chunk (l & 3) ^ ((l >> 3) & 3)
+    const int arow = 32 * wave + (lane >> 2);
+    const uint32_t achunk = (uint32_t)(8 * ((lane & 3) ^ ((lane >> 3) & 3)));  // elements
     __amdgpu_buffer_rsrc_t ra;
-    uint32_t va[4];
+    uint32_t va[2];
     if constexpr (GATHERED) {
         ra = make_rsrc(p.A, (uint32_t)((size_t)p.a_rows * Kd * ES));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = arow + 8 * i;
+        for (int i = 0; i < 2; ++i) {
+            const int r = arow + 16 * i;
             const int t = r < nvalid ? p.stok[row0 + r] : -1;
             va[i] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
         }
@@ -1049,7 +1060,7 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
         ra = make_rsrc(static_cast<const T *>(p.A) + (size_t)row0 * Kd,
                        (uint32_t)((size_t)nvalid * Kd * ES));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) va[i] = (uint32_t)(arow + 8 * i) * (uint32_t)Kd * ES;
+        for (int i = 0; i < 2; ++i) va[i] = (uint32_t)(arow + 16 * i) * (uint32_t)Kd * ES;
     }
 
     float4_t acc[2][kMT][kNpl];
@@ -1061,89 +1072,97 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
             for (int c = 0; c < kNpl; ++c) acc[m][mt][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     typedef __attribute__((address_space(3))) void *lds_ptr;
-    // the operands of step s into LDS buffer L; K chunks past Kd (the next
+    // the operands of K-step s into LDS buffer L; K chunks past Kd (the next
     // row's data) and steps past the end are read at offsets past the
     // descriptors' ranges, which return zeros
-    auto issue = [&](uint4 (&L)[kBigBufU4], int s) {
-        const uint32_t ka = (uint32_t)(64 * s) + achunk;
+    auto issue = [&](uint4 (&L)[kDeepBufU4], int s) {
+        const uint32_t ka = (uint32_t)(32 * s) + achunk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_ptr)(L + (32 * wave + 8 * i) * 8), 16,
+                ra, (lds_ptr)(L + (32 * wave + 16 * i) * 4), 16,
                 (int)ka < Kd ? va[i] + ka * ES : 0x80000000u, 0, 0, 0);
-        const uint32_t o = vb + (uint32_t)(2 * s + bhalf) * z.step_bytes;
+        const uint32_t o = vb + (uint32_t)s * z.step_bytes;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(L + bslot + 64 * j), 16,
-                                                     o + (uint32_t)j * 1024u, 0, 0, kNT);
+                                                     o + (uint32_t)j * 1024u, 0, 0, 0);
     };
-    struct Frag {
-        uint4 a[2][kMT];
-        uint4 b[2][2][kNpl];
-    };
-    auto read_a = [&](Frag &f, const uint4 (&L)[kBigBufU4], int h) {
+    uint4 fa[kMT], fb[2][kNpl];
+    auto read_a = [&](const uint4 (&L)[kDeepBufU4]) {
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             const int row = 64 * wr + 16 * mt + nq;
-            f.a[h][mt] = L[row * 8 + ((4 * h + kg) ^ (nq & 7))];
+            fa[mt] = L[row * 4 + (kg ^ ((row >> 1) & 3))];
         }
     };
-    auto read_b = [&](Frag &f, const uint4 (&L)[kBigBufU4], int h, int m, int c) {
-        f.b[h][m][c] = L[bidx(h, m, c)];
+    // B operand (matrix or slice half m, column quad c) of this wavefront
+    auto read_b = [&](const uint4 (&L)[kDeepBufU4], int m, int c) {
+        fb[m][c] = L[kDeepAU4 + (GATEUP ? 512 * m + 256 * wc : 512 * wc + 256 * m) + 64 * c + lane];
     };
-    // Step s with operands f: the loads of step s+2 go to Lf (step s's buffer,
-    // whose reads were complete at the last barrier), step s+1's operands are
-    // read from Ln into f as their registers free up; then every read done
-    // and this wavefront's loads landed (the barrier's fence), barrier
-    const int nst = z.nst;  // 32-wide MFMA steps
-    const int nsteps = (nst + 1) / 2;
-    Frag f;
-    auto stepfn = [&](int s, const uint4 (&Ln)[kBigBufU4], uint4 (&Lf)[kBigBufU4]) {
-        issue(Lf, s + 2);
+    // step s: loads of step s+NB-1 into Lf (read for step s-1, complete before
+    // the last barrier), MFMAs of step s with step s+1's operands read from Ln
+    // into the registers as they free up, then this wavefront's loads of step
+    // s+2 landed, barrier
+    auto stepfn = [&](int s, const uint4 (&Ln)[kDeepBufU4], uint4 (&Lf)[kDeepBufU4]) {
+        issue(Lf, s + NB - 1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int c = 0; c < kNpl; ++c)
 #pragma unroll
-            for (int c = 0; c < kNpl; ++c)
+            for (int m = 0; m < 2; ++m) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    if (2 * s + h < nst) {  // K tail: the tall cells run no such step
-#pragma unroll
-                        for (int mt = 0; mt < kMT; ++mt)
-                            acc[m][mt][c] = Elt<T>::mfma(f.a[h][mt], f.b[h][m][c], acc[m][mt][c]);
-                    }
-                    read_b(f, Ln, h, m, c);
-                    // keep this order: a read hoisted above the MFMAs would
-                    // hold a second set of operand registers
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            read_a(f, Ln, h);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __syncthreads();
+                for (int mt = 0; mt < kMT; ++mt)
+                    acc[m][mt][c] = Elt<T>::mfma(fa[mt], fb[m][c], acc[m][mt][c]);
+                read_b(Ln, m, c);
+                // keep this order: a read hoisted above the MFMAs would hold a
+                // second set of operand registers
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        read_a(Ln);
+        __builtin_amdgcn_s_waitcnt(wait_vm(VM));
+        asm volatile("s_barrier" ::: "memory");
     };
 
+    const int nst = z.nst;
     issue(L0, 0);
     issue(L1, 1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    issue(L2, 2);
+    if constexpr (NB == 5) issue(L3, 3);
+    __builtin_amdgcn_s_waitcnt(wait_vm(VM));  // steps 0 and 1 landed
+    asm volatile("s_barrier" ::: "memory");
+    read_a(L0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        read_a(f, L0, h);
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int c = 0; c < kNpl; ++c) read_b(f, L0, h, m, c);
-    }
-    __syncthreads();  // these reads done everywhere before step 2's loads reuse L0
-    // (no early exit from the unrolled loop: that made the compiler spill)
+        for (int c = 0; c < kNpl; ++c) read_b(L0, m, c);
+    // (no early exits from the unrolled loop: they made the compiler spill)
     int s = 0;
-    for (; s + 2 <= nsteps; s += 2) {
-        stepfn(s, L1, L0);
-        stepfn(s + 1, L0, L1);
+    if constexpr (NB == 5) {
+        for (; s + 5 <= nst; s += 5) {
+            stepfn(s, L1, L4);
+            stepfn(s + 1, L2, L0);
+            stepfn(s + 2, L3, L1);
+            stepfn(s + 3, L4, L2);
+            stepfn(s + 4, L0, L3);
+        }
+        if (s < nst) stepfn(s, L1, L4);
+        if (s + 1 < nst) stepfn(s + 1, L2, L0);
+        if (s + 2 < nst) stepfn(s + 2, L3, L1);
+        if (s + 3 < nst) stepfn(s + 3, L4, L2);
+    } else {
+        for (; s + 4 <= nst; s += 4) {
+            stepfn(s, L1, L3);
+            stepfn(s + 1, L2, L0);
+            stepfn(s + 2, L3, L1);
+            stepfn(s + 3, L0, L2);
+        }
+        if (s < nst) stepfn(s, L1, L3);
+        if (s + 1 < nst) stepfn(s + 1, L2, L0);
+        if (s + 2 < nst) stepfn(s + 2, L3, L1);
     }
-    if (s < nsteps) stepfn(s, L1, L0);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no load into LDS in flight at exit
     const int col = BCOLS * cb + (BCOLS / 2) * wc + kNpl * nq;
-    store_cells<T, GATEUP, kMT>(p, it, col, kg, acc, my_rinfo, 0);
+    store_cells<T, GATEUP, kMT, false>(p, it, col, kg, acc, my_rinfo, 0);
 }
 
 // ---- split-K reductions (fixed split order) --------------------------------
