@@ -100,6 +100,10 @@ struct Rec {
     }
 };
 
+// the work list puts the runs of 4 first when a big-cell kernel takes them
+// (packed weights, 16-bit, shape as ffn_shape decides)
+bool runs_first(const moe::FfnShape &z, bool packed) { return packed && (z.big_gu || z.big_dn); }
+
 bool timer_room(const moe_timer_t *t)
 {
     if (!t) return true;
@@ -113,7 +117,7 @@ bool timer_room(const moe_timer_t *t)
 int plan_impl(const int32_t *ids, const float *w, int T, int K, int E, int tm, int32_t *cnt,
               int32_t *eoff, int32_t *tiles, int32_t *stok, float *sw, int32_t *pos, int32_t *boff,
               int32_t *meta, void *scratch, size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr,
-              void *ffn_scratch = nullptr, bool *items_done = nullptr)
+              void *ffn_scratch = nullptr, bool *items_done = nullptr, bool runs_first = false)
 {
     moe_plan_sizes_t z;
     const int rc = plan_sizes(T, K, E, tm, &z);
@@ -130,7 +134,8 @@ int plan_impl(const int32_t *ids, const float *w, int T, int K, int E, int tm, i
         Rec r(tmr, s, MOE_STAGE_PLACE);
         const int64_t max_items = moe::ffn_max_items(E, tm, z.max_rows);
         if (moe::launch_plan_fused(ids, w, nent, E, K, tm, nblk, cnt, eoff, boff, tiles, stok, sw,
-                                   pos, meta, ffn_scratch, max_items, z.max_rows, s) != hipSuccess)
+                                   pos, meta, ffn_scratch, max_items, z.max_rows, runs_first,
+                                   s) != hipSuccess)
             return MOE_EHIP;
         if (items_done) *items_done = ffn_scratch != nullptr;
         return MOE_OK;
@@ -181,7 +186,8 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
     if (!have_items) {
         Rec r(tmr, s, MOE_STAGE_WORKLIST);
-        if (moe::launch_worklist(eoff, E, max_rows, scratch, z.max_items, s) != hipSuccess)
+        if (moe::launch_worklist(eoff, E, max_rows, scratch, z.max_items, runs_first(z, packed),
+                                 s) != hipSuccess)
             return MOE_EHIP;
     }
     {
@@ -258,9 +264,10 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     auto i32 = [&](size_t off) { return reinterpret_cast<int32_t *>(b + off); };
     auto f32 = [&](size_t off) { return reinterpret_cast<float *>(b + off); };
     bool items = false;
+    const moe::FfnShape fz = moe::ffn_shape(E, tm, z.max_rows, d, f, dtype);
     rc = plan_impl(ids, w, T, K, E, tm, i32(L.cnt), i32(L.eoff), i32(L.tiles), i32(L.stok),
                    f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
-                   z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items);
+                   z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items, runs_first(fz, packed));
     if (rc != MOE_OK) return rc;
     // The gate/up kernel gathers its rows from x itself when x is addressable
     // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
@@ -271,7 +278,7 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     }
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
-                  moe::ffn_shape(E, tm, z.max_rows, d, f, dtype).scratch_bytes, s, tmr, items,
+                  fz.scratch_bytes, s, tmr, items,
                   fused_gather ? x : nullptr, T, packed);
     if (rc != MOE_OK) return rc;
     return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);

@@ -22,7 +22,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // The grouped FFN works on items of at most kItemRows rows of one expert; its
 // scratch holds ctl (first kCtlBytes: ctl[0] = items, ctl[1] = items in runs
-// of 4) followed by the items.
+// of 4 when they come first in the list, else 0) followed by the items.
 constexpr int kItemRows = 64;
 constexpr size_t kCtlBytes = 256;
 
@@ -49,13 +49,18 @@ __host__ __device__ inline int32_t item_run(int q, int n)
     return 1;
 }
 
-// Position of item q of an expert's n items in the work list. The items in
-// runs of 4 of every expert come first, in ascending expert order, then the
-// remaining items (runs of 2 and single items), also by expert. qbefore and
-// rbefore count the items of lower experts in each part; quad_items is the
-// number of items in runs of 4 over all experts.
-__host__ __device__ inline int item_slot(int q, int n, int qbefore, int rbefore, int quad_items)
+// Position of item q of an expert's n items in the work list. qbefore and
+// rbefore count the items of lower experts in runs of 4 and not; quad_items
+// is the number of items in runs of 4 over all experts. With runs_first (when
+// the big-cell kernel takes the runs of 4) the items in runs of 4 of every
+// expert come first, in ascending expert order, then the remaining items
+// (runs of 2 and single items), also by expert; otherwise each expert's items
+// are together, in ascending expert order (its runs then sit next to its other
+// items, which read the same weights: better for L2 when one kernel takes all).
+__host__ __device__ inline int item_slot(int q, int n, int qbefore, int rbefore, int quad_items,
+                                         bool runs_first)
 {
+    if (!runs_first) return qbefore + rbefore + q;
     const int n4 = n & ~3;
     return q < n4 ? qbefore + q : quad_items + rbefore + (q - n4);
 }
@@ -83,6 +88,68 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
         if (lane >= o) v += u;
     }
     return v;
+}
+
+// Per-expert output ranges: lane l owns expert `expert` (its value in lane l)
+// with n entries. Each lane writes the first kOwnEntries entries of its own
+// expert; the rest of a heavy expert's entries are written by the whole
+// wavefront, heavy expert after heavy expert, lane q writing entries
+// kOwnEntries + q, + 64, ..., so that they are not written by one lane alone.
+// Every lane of the wavefront must call these (n = 0 for lanes without an
+// expert); the shuffles run with every lane active.
+constexpr int kOwnEntries = 8;
+
+// tiles[t0 + j] = expert for j < n
+__device__ __forceinline__ void wave_fill_tiles(int t0, int n, int expert, int lane,
+                                                int32_t *__restrict__ tiles)
+{
+    for (int q = 0; q < n && q < kOwnEntries; ++q) tiles[t0 + q] = expert;
+    uint64_t heavy = __ballot(n > kOwnEntries);
+    while (heavy) {
+        const int src = __ffsll((unsigned long long)heavy) - 1;
+        heavy &= heavy - 1;
+        const int ns = __shfl(n, src), ts = __shfl(t0, src), ex = __shfl(expert, src);
+        for (int q = kOwnEntries + lane; q < ns; q += kWave) tiles[ts + q] = ex;
+    }
+}
+
+// work item q of an expert with n items whose rows are [r0, r0 + rows), at its
+// work-list slot; items starting at or past max_rows are dropped and rows are
+// cut at max_rows (a plan within its bound reaches neither)
+__device__ __forceinline__ void put_item(int q, int n, int r0, int rows, int qbefore, int rbefore,
+                                         int quad_items, bool runs_first, int expert,
+                                         int max_items, int max_rows, WorkItem *__restrict__ items)
+{
+    const int idx = item_slot(q, n, qbefore, rbefore, quad_items, runs_first);
+    const int row = r0 + q * kItemRows;
+    if (idx < max_items && row < max_rows) {
+        WorkItem it;
+        it.expert = expert;
+        it.row0 = row;
+        it.nrows = min(min(kItemRows, rows - q * kItemRows), max_rows - row);
+        it.run = item_run(q, n);
+        items[idx] = it;
+    }
+}
+
+__device__ __forceinline__ void wave_fill_items(int n, int r0, int rows, int qbefore, int rbefore,
+                                                int quad_items, bool runs_first, int expert,
+                                                int lane, int max_items, int max_rows,
+                                                WorkItem *__restrict__ items)
+{
+    for (int q = 0; q < n && q < kOwnEntries; ++q)
+        put_item(q, n, r0, rows, qbefore, rbefore, quad_items, runs_first, expert, max_items,
+                 max_rows, items);
+    uint64_t heavy = __ballot(n > kOwnEntries);
+    while (heavy) {
+        const int src = __ffsll((unsigned long long)heavy) - 1;
+        heavy &= heavy - 1;
+        const int ns = __shfl(n, src), r0s = __shfl(r0, src), rs = __shfl(rows, src);
+        const int qb = __shfl(qbefore, src), rb = __shfl(rbefore, src), ex = __shfl(expert, src);
+        for (int q = kOwnEntries + lane; q < ns; q += kWave)
+            put_item(q, ns, r0s, rs, qb, rb, quad_items, runs_first, ex, max_items, max_rows,
+                     items);
+    }
 }
 
 // Workgroups of a 1-D grid are dealt to the 8 XCDs round-robin in blockIdx

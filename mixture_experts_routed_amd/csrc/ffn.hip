@@ -211,7 +211,8 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
 // to [0, max_rows] so that made-up offsets cannot lead outside the buffers.
 __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ eoff, int E,
                                                    int64_t max_rows, int32_t *__restrict__ ctl,
-                                                   WorkItem *__restrict__ items, int max_items)
+                                                   WorkItem *__restrict__ items, int max_items,
+                                                   int runs_first)
 {
     __shared__ int s_q[16], s_r[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -240,20 +241,11 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
         qtotal += s_q[q];
         rtotal += s_r[q];
     }
-    for (int q = 0; q < n; ++q) {
-        const int idx = item_slot(q, n, qbefore, rbefore, qtotal);
-        if (idx < max_items) {
-            WorkItem it;
-            it.expert = tid;
-            it.row0 = r0 + q * kItemRows;
-            it.nrows = min(kItemRows, rows - q * kItemRows);
-            it.run = item_run(q, n);
-            items[idx] = it;
-        }
-    }
+    wave_fill_items(n, r0, rows, qbefore, rbefore, qtotal, runs_first != 0, tid, lane, max_items,
+                    (int)max_rows, items);
     if (tid == 0) {
         ctl[0] = min(qtotal + rtotal, max_items);
-        ctl[1] = min(qtotal, max_items) & ~3;
+        ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
     }
 }
 
@@ -1231,12 +1223,12 @@ __global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ p
 
 // ---- host launchers --------------------------------------------------------
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
-                           int64_t max_items, hipStream_t s)
+                           int64_t max_items, bool runs_first, hipStream_t s)
 {
     int32_t *ctl = static_cast<int32_t *>(scratch);
     WorkItem *items = reinterpret_cast<WorkItem *>(static_cast<char *>(scratch) + kCtlBytes);
     hipLaunchKernelGGL(k_worklist, dim3(1), dim3(1024), 0, s, eoff, E, max_rows, ctl, items,
-                       (int)max_items);
+                       (int)max_items, runs_first ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ int plan_fused_max_blocks();
 hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E, int K, int tm,
                              int nblk, int32_t *cnt, int32_t *eoff, int32_t *boff, int32_t *tiles,
                              int32_t *stok, float *sw, int32_t *pos, int32_t *meta,
-                             void *ffn_scratch, int64_t max_items, int64_t max_rows, hipStream_t s);
+                             void *ffn_scratch, int64_t max_items, int64_t max_rows,
+                             bool runs_first, hipStream_t s);
 
 // ---- router ----
 hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
@@ -60,8 +61,9 @@ struct FfnShape {
 };
 FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype);
 
+// runs_first: the items in runs of 4 first (item_slot), for the big cells
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
-                           int64_t max_items, hipStream_t s);
+                           int64_t max_items, bool runs_first, hipStream_t s);
 hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *xs,
                          const int32_t *stok, const void *wg, const void *wu, int d, int f,
                          const int32_t *meta, const void *scratch, void *h, hipStream_t s);

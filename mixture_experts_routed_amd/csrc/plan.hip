@@ -57,12 +57,12 @@ __global__ __launch_bounds__(kPlanBlock) void k_scan(
     int run = 0;
     if (tid < E) {
         int b = 0;
-        for (; b + 8 <= nblk; b += 8) {  // 8 independent loads in flight
-            int v[8];
+        for (; b + 32 <= nblk; b += 32) {  // 32 independent loads in flight
+            int v[32];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = bcnt[(size_t)(b + q) * E2 + tid];
+            for (int q = 0; q < 32; ++q) v[q] = bcnt[(size_t)(b + q) * E2 + tid];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < 32; ++q) {
                 boff[(size_t)(b + q) * E + tid] = run;
                 run += v[q];
             }
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_scan(
             stok[r] = -1;
             sw[r] = 0.0f;
         }
-        for (int j = start / tm; j < (start + rows) / tm; ++j) tiles[j] = tid;
     }
+    wave_fill_tiles(start / tm, tid < E ? rows / tm : 0, tid, lane, tiles);
     if (tid == 0) {
         int nact = 0, maxc = 0, nskip = 0, nbad = 0;
 #pragma unroll
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     int nbits, int32_t *__restrict__ cnt, int32_t *__restrict__ eoff, int32_t *__restrict__ boff,
     int32_t *__restrict__ tiles, int32_t *__restrict__ stok, float *__restrict__ sw,
     int32_t *__restrict__ pos, int32_t *__restrict__ meta, int32_t *__restrict__ ctl,
-    WorkItem *__restrict__ items, int max_items, int max_rows)
+    WorkItem *__restrict__ items, int max_items, int max_rows, int runs_first)
 {
     __shared__ int s_tot[kMaxExperts], s_before[kMaxExperts], s_eoff[kMaxExperts];
     __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
@@ -298,22 +298,11 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
                 stok[r] = -1;
                 sw[r] = 0.0f;
             }
-            for (int j = start / tm; j < (start + rows) / tm; ++j) tiles[j] = tid;
-            if (items) {
-                for (int q = 0; q < nit; ++q) {
-                    const int idx = item_slot(q, nit, qbefore, rbefore, qtotal);
-                    const int r0 = start + q * kItemRows;
-                    if (idx < max_items && r0 < max_rows) {
-                        WorkItem it;
-                        it.expert = tid;
-                        it.row0 = r0;
-                        it.nrows = min(min(kItemRows, rows - q * kItemRows), max_rows - r0);
-                        it.run = item_run(q, nit);
-                        items[idx] = it;
-                    }
-                }
-            }
         }
+        wave_fill_tiles(start / tm, tid < E ? rows / tm : 0, tid, lane, tiles);
+        if (items)  // rows past max_rows (not reached by a plan within its bound) are dropped
+            wave_fill_items(tid < E ? nit : 0, start, rows, qbefore, rbefore, qtotal,
+                            runs_first != 0, tid, lane, max_items, max_rows, items);
         if (tid == 0) {
             int nact = 0, maxc = 0, nskip = 0, nbad = 0;
 #pragma unroll
@@ -337,7 +326,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             meta[kMetaK] = K;
             if (items) {
                 ctl[0] = min(qtotal + rtotal, max_items);
-                ctl[1] = min(qtotal, max_items) & ~3;
+                ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
             }
         }
     }
@@ -373,7 +362,8 @@ int plan_fused_max_blocks() { return kFusedMaxBlocks; }
 hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E, int K, int tm,
                              int nblk, int32_t *cnt, int32_t *eoff, int32_t *boff, int32_t *tiles,
                              int32_t *stok, float *sw, int32_t *pos, int32_t *meta,
-                             void *ffn_scratch, int64_t max_items, int64_t max_rows, hipStream_t s)
+                             void *ffn_scratch, int64_t max_items, int64_t max_rows,
+                             bool runs_first, hipStream_t s)
 {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
@@ -383,7 +373,7 @@ hipError_t launch_plan_fused(const int32_t *ids, const float *w, int nent, int E
                                   : nullptr;
     hipLaunchKernelGGL(k_plan_fused, dim3(nblk), dim3(kPlanBlock), 0, s, ids, w, nent, E, K, tm,
                        nbits, cnt, eoff, boff, tiles, stok, sw, pos, meta, ctl, items,
-                       (int)max_items, (int)max_rows);
+                       (int)max_items, (int)max_rows, runs_first ? 1 : 0);
     return hipGetLastError();
 }
 

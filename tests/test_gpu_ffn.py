@@ -134,13 +134,14 @@ def test_ffn_launch_paths(cfg, sgu, sdn, tall):
     run_ffn(case, case.ids, case.w, case.x)
 
 
-def worklist_model(eoff, E, max_rows):
+def worklist_model(eoff, E, max_rows, runs_first=True):
     """The grouped FFN's work list as the header describes it: each expert's
     rows cut into items of 64; per expert runs of 4 items first, then a run of
     2 if at least 2 items remain, then single items; the items in runs of 4 of
     all experts come first (ascending expert), then the others (ascending
-    expert); run = length | index << 8. Returns (items [n, 4], items in runs of
-    4)."""
+    expert), or, without runs_first, each expert's items together by expert;
+    run = length | index << 8. Returns (items [n, 4], items in runs of 4 when
+    they come first, else 0)."""
     quad, rest = [], []
     for e in range(E):
         a = min(max(int(eoff[e]), 0), max_rows)
@@ -154,8 +155,9 @@ def worklist_model(eoff, E, max_rows):
                 run = 2 | ((q - n4) << 8)
             else:
                 run = 1
-            (quad if q < n4 else rest).append((e, a + 64 * q, min(64, b - a - 64 * q), run))
-    return np.array(quad + rest, np.int32).reshape(-1, 4), len(quad)
+            (quad if q < n4 or not runs_first else rest).append(
+                (e, a + 64 * q, min(64, b - a - 64 * q), run))
+    return np.array(quad + rest, np.int32).reshape(-1, 4), len(quad) if runs_first else 0
 
 
 WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3, f=64,
@@ -164,23 +166,27 @@ WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3
 
 @pytest.mark.parametrize("cfg", WL, ids=[c.name for c in WL])
 @pytest.mark.parametrize("fused", [False, True], ids=["moe_expert_ffn", "moe_forward"])
-def test_worklist_layout(cfg, fused):
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_worklist_layout(cfg, fused, packed):
     """the work list the FFN kernels consume (written by the worklist kernel
     for moe_expert_ffn, by the one-launch plan for moe_forward) equals the
-    model above"""
+    model above; the runs of 4 come first only where the big-cell kernels take
+    them"""
     ids, w = synth.routing(cfg)
     T, K = ids.shape
     p = oracle.plan(ids, w, cfg.E, cfg.tm)
     z = abi.moe_plan_sizes(T, K, cfg.E, cfg.tm)
     R = z.max_rows
     dt = abi.DTYPE_NAME[cfg.dtype]
-    want, nfour = worklist_model(p["eoff"], cfg.E, R)
-    say(f"[worklist] {cfg.name} {'forward' if fused else 'expert_ffn'}")
+    first = packed and abi.moe_ffn_big_cells(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt) != 0
+    want, nfour = worklist_model(p["eoff"], cfg.E, R, first)
+    say(f"[worklist] {cfg.name} {'forward' if fused else 'expert_ffn'} packed={packed}")
+    wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
+           for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
+    pk = abi.pack(*wts) if packed else None
     if fused:
         x = torch.zeros((T, cfg.d), dtype=TORCH16[cfg.dtype], device="cuda")
-        wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
-               for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
-        _, ws = abi.forward(x, dev(ids), dev(w), *wts, tm=cfg.tm)
+        _, ws = abi.forward(x, dev(ids), dev(w), *wts, tm=cfg.tm, packed=pk)
         L = abi.moe_forward_layout(T, K, cfg.E, cfg.d, cfg.f, cfg.tm, dt)
         scratch = ws[L.ffn_scratch:]
     else:
@@ -194,10 +200,12 @@ def test_worklist_layout(cfg, fused):
         xs = torch.zeros((R, cfg.d), dtype=TORCH16[cfg.dtype], device="cuda")
         h = torch.empty((R, cfg.f), dtype=TORCH16[cfg.dtype], device="cuda")
         y = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
-        wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
-               for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
-        abi.moe_expert_ffn(xs, *wts, dt, cfg.E, cfg.d, cfg.f, cfg.tm, dev(p["eoff"]), dev(stok),
-                           dev(sw), dev(p["meta"]), R, h, y, scratch)
+        args = (dt, cfg.E, cfg.d, cfg.f, cfg.tm, dev(p["eoff"]), dev(stok), dev(sw),
+                dev(p["meta"]), R, h, y, scratch)
+        if packed:
+            abi.moe_expert_ffn_packed(xs, pk["gate"], pk["up"], pk["down"], *args)
+        else:
+            abi.moe_expert_ffn(xs, *wts, *args)
     torch.cuda.synchronize()
     raw = scratch[: 256 + 16 * len(want)].cpu().numpy().view(np.int32)
     assert raw[0] == len(want) and raw[1] == nfour
