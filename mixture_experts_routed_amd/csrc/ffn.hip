@@ -949,11 +949,11 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
 // y) on 512 threads, in 32-wide K-steps:
 //  * a step's operands (A: 256 rows x 64 bytes; B: the 4 KB packed tiles of
 //    slices w0, w0+1, already in MFMA lane order) go straight from memory into
-//    one of NB LDS buffers of 32 KB (buffer loads with the LDS flag, no
-//    registers), NB - 1 steps ahead of the MFMAs, and are waited for 2 steps
-//    (gate/up, NB = 5: the whole LDS) or 1 step (down, NB = 4, plus the rows'
-//    router weights) before use: these loads spend about as long in the memory
-//    system as a step's MFMAs take;
+//    one of 5 LDS buffers of 32 KB (the whole LDS; buffer loads with the LDS
+//    flag, no registers), 4 steps ahead of the MFMAs, and are waited for 2
+//    steps before use: these loads spend about as long in the memory system as
+//    a step's MFMAs take (the down epilogue's router weights are loaded into
+//    registers at the start instead of LDS);
 //  * the loads keep the default cache policy: the operands of a step are read
 //    by several workgroups at about the same time (the rows by every column
 //    block of the run, the weights by the runs of the same expert), which then
@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
 //  * wavefront (wr, wc) computes rows 64*wr.. of the run and packed slice
 //    w0 + wc: the same 2 x 4 x 4 accumulators, MFMA sequence and epilogue as
 //    a tall cell, so the results are the same bits.
-// The buffers are separate LDS arrays and the step loop is unrolled by NB, so
+// The buffers are separate LDS arrays and the step loop is unrolled by 5, so
 // that the compiler can tell a buffer's reads from the loads in flight into
 // the others and does not make the reads wait for those loads.
 constexpr int kBigThreads = 512;
@@ -986,11 +986,10 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     static_assert(GATEUP || !GATHERED, "the down projection reads h row-major");
     constexpr int ES = 2;
     constexpr int BCOLS = big_cols(GATEUP);
-    constexpr int NB = GATEUP ? 5 : 4;        // LDS buffers
+    constexpr int NB = 5;                     // LDS buffers
     constexpr int VM = 4 * (NB - 3);          // loads of this wavefront still in flight
     __shared__ uint4 L0[kDeepBufU4], L1[kDeepBufU4], L2[kDeepBufU4], L3[kDeepBufU4],
-        L4[GATEUP ? kDeepBufU4 : 1];
-    __shared__ float2 rinfo[GATEUP ? 1 : 4 * kItemRows];
+        L4[kDeepBufU4];
     const int Kd = p.Kd, N = p.N;
     const int ncb = (N + BCOLS - 1) / BCOLS;
     const int nquads = min(ctl[1], ctl[0]) / 4;
@@ -1011,8 +1010,19 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     const int wr = wave & 3, wc = wave >> 2;
     const int nq = lane & 15, kg = lane >> 4;
     const WorkItem it = items[4 * qd + wr];
-    float2 *my_rinfo = GATEUP ? nullptr : rinfo + kItemRows * wr;
-    if (!GATEUP && wc == 0) load_rinfo<true>(p, it, lane, my_rinfo);
+    // down: the router weight and token of the item's row 16 mt + 4 kg + r,
+    // with (mt, r) = (nq >> 2, nq & 3), loaded now so that they have landed by
+    // the epilogue; the 16 lanes of a K-group hold the 16 rows that each of
+    // them stores (taken there with a shuffle), one register each
+    float rsw = 0.f;
+    int rtok = -1;
+    if constexpr (!GATEUP) {
+        const int rl = 16 * (nq >> 2) + 4 * kg + (nq & 3);
+        if (rl < it.nrows) {
+            rsw = p.sw[(int64_t)it.row0 + rl];
+            rtok = p.stok[(int64_t)it.row0 + rl];
+        }
+    }
 
     // B: per step the packed tiles of slices w0, w0+1: gate/up 8 KB of gate,
     // then 8 KB of up; down 16 KB (tiles (w0, 0), (w0, 1), (w0+1, 0),
@@ -1092,7 +1102,7 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     auto read_b = [&](const uint4 (&L)[kDeepBufU4], int m, int c) {
         fb[m][c] = L[kDeepAU4 + (GATEUP ? 512 * m + 256 * wc : 512 * wc + 256 * m) + 64 * c + lane];
     };
-    // step s: loads of step s+NB-1 into Lf (read for step s-1, complete before
+    // step s: loads of step s+4 into Lf (read for step s-1, complete before
     // the last barrier), MFMAs of step s with step s+1's operands read from Ln
     // into the registers as they free up, then this wavefront's loads of step
     // s+2 landed, barrier
@@ -1119,7 +1129,7 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     issue(L0, 0);
     issue(L1, 1);
     issue(L2, 2);
-    if constexpr (NB == 5) issue(L3, 3);
+    issue(L3, 3);
     __builtin_amdgcn_s_waitcnt(wait_vm(VM));  // steps 0 and 1 landed
     asm volatile("s_barrier" ::: "memory");
     read_a(L0);
@@ -1129,32 +1139,45 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
         for (int c = 0; c < kNpl; ++c) read_b(L0, m, c);
     // (no early exits from the unrolled loop: they made the compiler spill)
     int s = 0;
-    if constexpr (NB == 5) {
-        for (; s + 5 <= nst; s += 5) {
-            stepfn(s, L1, L4);
-            stepfn(s + 1, L2, L0);
-            stepfn(s + 2, L3, L1);
-            stepfn(s + 3, L4, L2);
-            stepfn(s + 4, L0, L3);
-        }
-        if (s < nst) stepfn(s, L1, L4);
-        if (s + 1 < nst) stepfn(s + 1, L2, L0);
-        if (s + 2 < nst) stepfn(s + 2, L3, L1);
-        if (s + 3 < nst) stepfn(s + 3, L4, L2);
-    } else {
-        for (; s + 4 <= nst; s += 4) {
-            stepfn(s, L1, L3);
-            stepfn(s + 1, L2, L0);
-            stepfn(s + 2, L3, L1);
-            stepfn(s + 3, L0, L2);
-        }
-        if (s < nst) stepfn(s, L1, L3);
-        if (s + 1 < nst) stepfn(s + 1, L2, L0);
-        if (s + 2 < nst) stepfn(s + 2, L3, L1);
+    for (; s + 5 <= nst; s += 5) {
+        stepfn(s, L1, L4);
+        stepfn(s + 1, L2, L0);
+        stepfn(s + 2, L3, L1);
+        stepfn(s + 3, L4, L2);
+        stepfn(s + 4, L0, L3);
     }
+    if (s < nst) stepfn(s, L1, L4);
+    if (s + 1 < nst) stepfn(s + 1, L2, L0);
+    if (s + 2 < nst) stepfn(s + 2, L3, L1);
+    if (s + 3 < nst) stepfn(s + 3, L4, L2);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no load into LDS in flight at exit
     const int col = BCOLS * cb + (BCOLS / 2) * wc + kNpl * nq;
-    store_cells<T, GATEUP, kMT, false>(p, it, col, kg, acc, my_rinfo, 0);
+    if constexpr (GATEUP) {
+        store_cells<T, true, kMT, false>(p, it, col, kg, acc, nullptr, 0);
+    } else {
+        // y = router weight x accumulator (fp32) on rows holding an entry, as
+        // store_cells does, through a descriptor over the item's rows (the
+        // shuffles run with every lane of the wavefront active)
+        constexpr int HALF = 16 * kNpl;
+        const __amdgpu_buffer_rsrc_t ry =
+            make_rsrc(static_cast<float *>(p.out) + (int64_t)it.row0 * N, (uint32_t)(it.nrows * N * 4));
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int src = 16 * kg + 4 * mt + r;
+                const float g = __shfl(rsw, src);
+                if (__shfl(rtok, src) < 0) continue;  // pad rows (and rows past the item)
+                const int rl = 16 * mt + 4 * kg + r;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (col + m * HALF >= N) continue;  // col + HALF < N implies col < N
+                    const float4 v = make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
+                                                 g * acc[m][mt][2][r], g * acc[m][mt][3][r]);
+                    store_sc1(ry, (uint32_t)((rl * N + col + m * HALF) * 4), v);
+                }
+            }
+    }
 }
 
 // ---- split-K reductions (fixed split order) --------------------------------
