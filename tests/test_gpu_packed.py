@@ -39,6 +39,9 @@ BIG = [
     custom("big_cells_f16_16e", T=4096, d=256, E=16, K=4, f=512, dtype="f16", bias="zipf1.1"),
     custom("big_cells_bf16_24e", T=3000, d=264, E=24, K=3, f=136, dtype="bf16",
            bias="normal0.5"),
+    # fewer 32-wide K-steps than the kernel keeps in flight (gate/up 3, down 2)
+    custom("big_cells_short_k_f16", T=2048, d=96, E=4, K=2, f=40, dtype="f16", bias="zipf1.1",
+           x_std=1.0),
 ]
 CASES += BIG
 
