@@ -299,10 +299,11 @@ __device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
 // (its y reads then hit the Infinity Cache). Default-policy stores were slower
 // than both, and sc1 stores of the gate/up output h gained nothing.
 constexpr int kSC1 = 16;
+template <int POLICY = kSC1>
 __device__ __forceinline__ void store_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v)
 {
     typedef unsigned u4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kSC1);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, POLICY);
 }
 
 // ---- per element type: MFMA and conversion -------------------------------
@@ -1157,7 +1158,11 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     } else {
         // y = router weight x accumulator (fp32) on rows holding an entry, as
         // store_cells does, through a descriptor over the item's rows (the
-        // shuffles run with every lane of the wavefront active)
+        // shuffles run with every lane of the wavefront active). Non-temporal
+        // here: at the shapes that take big cells y is far larger than the
+        // caches, and sc1 stores evicted the operands that the other
+        // workgroups share in L2 (measured: down 1.83 -> 1.67 ms on the
+        // one-call long prompt)
         constexpr int HALF = 16 * kNpl;
         const __amdgpu_buffer_rsrc_t ry =
             make_rsrc(static_cast<float *>(p.out) + (int64_t)it.row0 * N, (uint32_t)(it.nrows * N * 4));
@@ -1174,7 +1179,7 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
                     if (col + m * HALF >= N) continue;  // col + HALF < N implies col < N
                     const float4 v = make_float4(g * acc[m][mt][0][r], g * acc[m][mt][1][r],
                                                  g * acc[m][mt][2][r], g * acc[m][mt][3][r]);
-                    store_sc1(ry, (uint32_t)((rl * N + col + m * HALF) * 4), v);
+                    store_sc1<kNT>(ry, (uint32_t)((rl * N + col + m * HALF) * 4), v);
                 }
             }
     }
