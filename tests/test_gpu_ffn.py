@@ -30,19 +30,26 @@ def run_ffn(case, ids, w, x, entries=None):
     sw = np.zeros(R, np.float32)
     sw[:nr] = p["sw"]
     es = synth.ELEM_BYTES[cfg.dtype]
-    h = polluted(R * cfg.f * es // 4)
-    y = polluted(R * cfg.d, torch.float32)
-    scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R,
-                                                    abi.DTYPE_NAME[cfg.dtype]),
-                          dtype=torch.uint8, device="cuda")
+    # scratch starts as garbage (the call must not rely on its contents: the
+    # work list and the split-K partial sums are rewritten on every call), and
+    # the second call on the same scratch must give the same bits
+    scratch = polluted(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R,
+                                                 abi.DTYPE_NAME[cfg.dtype]) // 4 + 1)
     say(f"[ffn] {cfg.name}: T={T} d={cfg.d} E={cfg.E} K={K} f={cfg.f} {cfg.dtype} tm={cfg.tm} "
         f"nr={nr}")
-    abi.moe_expert_ffn(dev(xs, cfg.dtype), case.d("wg"), case.d("wu"), case.d("wd"),
-                       abi.DTYPE_NAME[cfg.dtype], cfg.E, cfg.d, cfg.f, cfg.tm, dev(p["eoff"]),
-                       dev(stok), dev(sw), dev(p["meta"]), R, h, y, scratch)
-    torch.cuda.synchronize()
-    hh = host(h).view(np.uint16 if es == 2 else np.float32).reshape(R, cfg.f)
-    yy = host(y).reshape(R, cfg.d)
+    outs = []
+    for _ in range(2):
+        h = polluted(R * cfg.f * es // 4)
+        y = polluted(R * cfg.d, torch.float32)
+        abi.moe_expert_ffn(dev(xs, cfg.dtype), case.d("wg"), case.d("wu"), case.d("wd"),
+                           abi.DTYPE_NAME[cfg.dtype], cfg.E, cfg.d, cfg.f, cfg.tm, dev(p["eoff"]),
+                           dev(stok), dev(sw), dev(p["meta"]), R, h, y, scratch)
+        torch.cuda.synchronize()
+        outs.append((host(h), host(y)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    hh = outs[0][0].view(np.uint16 if es == 2 else np.float32).reshape(R, cfg.f)
+    yy = outs[0][1].reshape(R, cfg.d)
     flat = ids.reshape(-1)
     valid = np.nonzero((flat >= 0) & (flat < cfg.E))[0]
     if entries is None:

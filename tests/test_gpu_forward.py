@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, abi, chunk_of, custom, dev, host, make_case, rel_err, say, synth
+from gpu_util import (TOL, abi, chunk_of, custom, dev, host, make_case, polluted, rel_err, say,
+                      synth)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,12 +115,20 @@ def test_forward_long_prompt_all_chunks():
                                  PATHS[-1]], ids=["prefill_fp16", "decode_bf16_split",
                                                   "tall_split_unit_bf16"])
 def test_forward_deterministic(cfg):
-    """bitwise equal on a second call (split-K partials are added in a fixed order)"""
+    """bitwise equal on a second call (split-K partials are added in a fixed
+    order), the first call on a workspace full of garbage (the plan rewrites the
+    FFN's work list), and the result against the oracle"""
     case = make_case(cfg)
     say(f"[forward determinism] {cfg.name}")
-    a, ws = gpu_forward(case, case.ids, case.w, case.x)
+    need = abi.moe_forward_workspace(cfg.T, cfg.K, cfg.E, cfg.d, cfg.f, cfg.tm,
+                                     abi.DTYPE_NAME[cfg.dtype])
+    a, ws = gpu_forward(case, case.ids, case.w, case.x, polluted(need // 4 + 1).view(torch.uint8))
     b, _ = gpu_forward(case, case.ids, case.w, case.x, ws)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    toks = np.unique(np.linspace(0, cfg.T - 1, min(cfg.T, 24)).astype(np.int32))
+    ref = oracle.ffn(case.x, case.ids, case.w, case.wg, case.wu, case.wd, cfg.dtype, True,
+                     tokens=toks)
+    assert rel_err(a[toks], ref.astype(np.float32)) <= TOL[cfg.dtype]
     case.drop_device()
 
 
