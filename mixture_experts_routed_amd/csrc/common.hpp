@@ -65,29 +65,48 @@ __host__ __device__ inline int item_slot(int q, int n, int qbefore, int rbefore,
     return q < n4 ? qbefore + q : quad_items + rbefore + (q - n4);
 }
 
-__device__ __forceinline__ int wave_sum(int v)
+// Wavefront scans and reductions on DPP lane moves (register to register,
+// no LDS round trip): within each row of 16 lanes, Hillis-Steele steps
+// row_shr 1, 2, 4, 8; then row_bcast 15 adds row 0's total to row 1 and row
+// 2's to row 3, and row_bcast 31 adds lane 31's (rows 0-1) to rows 2 and 3.
+// A lane whose source is outside its row, or whose row is masked off, takes
+// `id` (the operation's identity). Every lane of the wavefront must be active.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_move(int v, int id)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xf, false);
 }
-
-__device__ __forceinline__ int wave_max(int v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
+enum : int { kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143 };
 
 // inclusive prefix sum across the 64 lanes of a wave
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+__device__ __forceinline__ int wave_inclusive_scan(int v, int /*lane*/)
 {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_up(v, o);
-        if (lane >= o) v += u;
-    }
+    v += dpp_move<kRowShr + 1>(v, 0);
+    v += dpp_move<kRowShr + 2>(v, 0);
+    v += dpp_move<kRowShr + 4>(v, 0);
+    v += dpp_move<kRowShr + 8>(v, 0);
+    v += dpp_move<kRowBcast15, 0xa>(v, 0);
+    v += dpp_move<kRowBcast31, 0xc>(v, 0);
     return v;
+}
+
+// sum over the wave (the same value in every lane)
+__device__ __forceinline__ int wave_sum(int v)
+{
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(v, 0), kWave - 1);
+}
+
+// maximum over the wave (the same value in every lane)
+__device__ __forceinline__ int wave_max(int v)
+{
+    constexpr int lo = -2147483647 - 1;
+    v = max(v, dpp_move<kRowShr + 1>(v, lo));
+    v = max(v, dpp_move<kRowShr + 2>(v, lo));
+    v = max(v, dpp_move<kRowShr + 4>(v, lo));
+    v = max(v, dpp_move<kRowShr + 8>(v, lo));
+    v = max(v, dpp_move<kRowBcast15, 0xa>(v, lo));
+    v = max(v, dpp_move<kRowBcast31, 0xc>(v, lo));
+    return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
 // Per-expert output ranges: lane l owns expert `expert` (its value in lane l)

@@ -197,10 +197,14 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
 // into LDS -- per-expert totals and the counts of the blocks before b -- so it
 // knows the padded expert offsets and its own block offsets without waiting
 // for the other workgroups; then it places its own entries exactly as k_place
-// does. Workgroup 0 also writes the layer-wide outputs (cnt, eoff, tiles, pad
-// rows, meta) and, when asked, the grouped FFN's work list. The redundant
-// counting costs nblk * nent LDS atomics in total (20 x 20,480 at T=2048,
-// top-10), far less than two extra dependent launches.
+// does. The per-expert layer-wide outputs (cnt, eoff, pad rows, tiles and,
+// when asked, the grouped FFN's work items) of expert e are written by
+// workgroup e % nblk, so that no workgroup carries them all; workgroup 0
+// writes eoff[E], meta and the item count. The redundant counting costs
+// nblk * nent LDS atomics in total (20 x 20,480 at T=2048, top-10), far less
+// than two extra dependent launches. Each lane issues all its loads of ids
+// at once (at most kFusedMaxBlocks), and its own entry's id and router
+// weight before the counting, so that the placement does not wait for them.
 constexpr int kFusedMaxBlocks = 32;
 
 __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
@@ -215,34 +219,39 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x;
-    for (int e = tid; e < E; e += kPlanBlock) {
-        s_tot[e] = 0;
-        s_before[e] = 0;
-        wc[e] = make_uint4(0u, 0u, 0u, 0u);
+    const int bstart = b * kPlanBlock;
+    // this lane's own entry (placed in step 3)
+    const int i = bstart + tid;
+    const bool inb = i < nent;
+    const int e = inb ? ids[i] : -1;
+    const float wi = inb ? w[i] : 0.0f;
+    for (int q = tid; q < E; q += kPlanBlock) {
+        s_tot[q] = 0;
+        s_before[q] = 0;
+        wc[q] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
     // 1. histogram of all entries, and of the entries before this block
-    const int bstart = b * kPlanBlock;
     int skip = 0, bad = 0;
-    constexpr int U = 16;  // loads in flight per lane before their atomics
+    constexpr int U = kFusedMaxBlocks;  // every load of the lane in flight before its atomics
     for (int i0 = tid; i0 < nent; i0 += U * kPlanBlock) {
         int v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * kPlanBlock;
-            v[u] = i < nent ? ids[i] : -2;
+            const int j = i0 + u * kPlanBlock;
+            v[u] = j < nent ? ids[j] : -2;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * kPlanBlock;
-            const int e = v[u];
-            if ((unsigned)e < (unsigned)E) {
-                atomicAdd(&s_tot[e], 1);
-                if (i < bstart) atomicAdd(&s_before[e], 1);
-            } else if (i < nent) {
-                skip += (e == -1);
-                bad += (e != -1);
+            const int j = i0 + u * kPlanBlock;
+            const int ej = v[u];
+            if ((unsigned)ej < (unsigned)E) {
+                atomicAdd(&s_tot[ej], 1);
+                if (j < bstart) atomicAdd(&s_before[ej], 1);
+            } else if (j < nent) {
+                skip += (ej == -1);
+                bad += (ej != -1);
             }
         }
     }
@@ -290,8 +299,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         s_eoff[tid] = start;
         boff[(size_t)b * E + tid] = s_before[tid];
     }
-    if (b == 0) {
-        if (tid < E) {
+    {
+        // expert tid's layer-wide outputs, by workgroup tid % nblk
+        const bool mine = tid < E && tid % (int)gridDim.x == b;
+        if (mine) {
             cnt[tid] = c;
             eoff[tid] = start;
             for (int r = start + c; r < start + rows; ++r) {  // 0..tm-1 pad rows
@@ -299,11 +310,11 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
                 sw[r] = 0.0f;
             }
         }
-        wave_fill_tiles(start / tm, tid < E ? rows / tm : 0, tid, lane, tiles);
+        wave_fill_tiles(start / tm, mine ? rows / tm : 0, tid, lane, tiles);
         if (items)  // rows past max_rows (not reached by a plan within its bound) are dropped
-            wave_fill_items(tid < E ? nit : 0, start, rows, qbefore, rbefore, qtotal,
+            wave_fill_items(mine ? nit : 0, start, rows, qbefore, rbefore, qtotal,
                             runs_first != 0, tid, lane, max_items, max_rows, items);
-        if (tid == 0) {
+        if (b == 0 && tid == 0) {
             int nact = 0, maxc = 0, nskip = 0, nbad = 0;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
@@ -332,9 +343,6 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     }
 
     // 3. placement of this block's entries (as k_place, offsets from LDS)
-    const int i = bstart + tid;
-    const bool inb = i < nent;
-    const int e = inb ? ids[i] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
     uint64_t same = __ballot(valid);
     for (int p = 0; p < nbits; ++p) {
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         const int row = s_eoff[e] + s_before[e] + bytes_below(wc[e], wv) + rank;
         pos[i] = row;
         stok[row] = i / K;
-        sw[row] = w[i];
+        sw[row] = wi;
     } else if (inb) {
         pos[i] = -1;
     }
