@@ -530,7 +530,6 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
     constexpr int KSTEP = 4 * KR;
     constexpr int NMAT = 2;       // two B streams (see below)
     constexpr int LB = NPL * ES;  // bytes per lane per row
-    typedef typename Ld<LB>::type RowT;
     const T *A = static_cast<const T *>(p.A);
     const T *B0 = static_cast<const T *>(p.B0);
     const T *B1 = static_cast<const T *>(p.B1);
@@ -723,7 +722,6 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
     constexpr int HALF = GATEUP ? 0 : 16 * NPL;
     constexpr int LB = NPL * ES;
     constexpr int BUF = tall_buf_u4(C);
-    typedef typename Ld<LB>::type RowT;
     static_assert(H * C == 2 && RP * H == KR, "tall cell shape");
     const T *A = static_cast<const T *>(p.A);
     const T *B0 = static_cast<const T *>(p.B0);
