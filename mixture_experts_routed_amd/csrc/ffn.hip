@@ -154,8 +154,15 @@ namespace {
 // columns of one workgroup's 4 slices: gate/up 4 x 64, down 4 x 128
 int group_cols(bool gateup) { return kWavesPerBlock * (gateup ? 16 * kNpl : 32 * kNpl); }
 
-// Split-K is used when fewer than this many (item, column group) cells exist
-// at most: about two workgroups per CU.
+// Split-K is used when the bound on (item, column group) cells is below
+// kSplitBelowCells, three quarters of the 256 CUs: then each projection's
+// reduction is cut into enough K ranges for about kTargetCells workgroups,
+// two per CU. Above it, a split gains less than its reduction launch costs
+// (decode, 2,816 x 704 bf16: the down projection's 246 cells unsplit took
+// 29.7 us, split in two 27.1 us plus 4.6 us to reduce), while the gate/up
+// projection's 123 cells, each streaming 2.9 MB, take 51 us split 5 ways
+// (3: 54, 4: 52; 6 ways no longer fits one round of workgroups: 61).
+constexpr int64_t kSplitBelowCells = 192;
 constexpr int64_t kTargetCells = 512;
 // The 8-wavefront kernel takes the runs of 4 items when the plan bound allows
 // this many rows per expert on average.
@@ -167,7 +174,7 @@ void split_for(int64_t cells, int Kd, int kstep, int *nsplit, int *steps)
 {
     const int nsteps = (Kd + kstep - 1) / kstep;
     int s = 1;
-    if (cells < kTargetCells) s = (int)((kTargetCells + cells - 1) / cells);
+    if (cells < kSplitBelowCells) s = (int)((kTargetCells + cells - 1) / cells);
     s = s < kMaxSplit ? s : kMaxSplit;
     const int smax = nsteps / kMinStepsPerSplit > 1 ? nsteps / kMinStepsPerSplit : 1;
     s = s < smax ? s : smax;

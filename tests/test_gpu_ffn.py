@@ -124,7 +124,7 @@ PATHS = [
      True, True),
     (custom("tall_mix_f32", T=400, d=256, E=4, K=2, f=192, dtype="f32", bias="zipf1.1"), True,
      False, True),
-    (custom("tall_split_unit_f16", T=2048, d=512, E=8, K=2, f=1024, dtype="f16", bias="zipf1.1",
+    (custom("tall_split_unit_f16", T=1024, d=512, E=8, K=2, f=1024, dtype="f16", bias="zipf1.1",
             x_std=1.0), True, True, True),
 ]
 

@@ -54,7 +54,7 @@ PATHS = [
     custom("split_both_bf16", T=6, d=1536, E=64, K=4, f=1024, dtype="bf16"),
     custom("tall4_split_f16", T=600, d=2048, E=2, K=1, f=256, dtype="f16"),
     custom("tall_mix_f32", T=400, d=256, E=4, K=2, f=192, dtype="f32", bias="zipf1.1"),
-    custom("tall_split_unit_bf16", T=2048, d=512, E=8, K=2, f=1024, dtype="bf16",
+    custom("tall_split_unit_bf16", T=1024, d=512, E=8, K=2, f=1024, dtype="bf16",
            bias="zipf1.1", x_std=1.0),
     # T*K = 40,960 > 32,768: the plan runs as three launches and the work list
     # is written by its own kernel

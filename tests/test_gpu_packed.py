@@ -42,6 +42,9 @@ BIG = [
     # fewer 32-wide K-steps than the kernel keeps in flight (gate/up 3, down 2)
     custom("big_cells_short_k_f16", T=2048, d=96, E=4, K=2, f=40, dtype="f16", bias="zipf1.1",
            x_std=1.0),
+    # big gate/up cells next to a down projection split along f (few down cells)
+    custom("big_cells_split_down_f16", T=2048, d=256, E=4, K=2, f=2048, dtype="f16",
+           bias="zipf1.1"),
 ]
 CASES += BIG
 
