@@ -13,13 +13,16 @@
 // -index) -- an order-preserving image of the float in the high word, the
 // inverted index in the low word -- so the winner is the largest logit and, on
 // equal logits, the lowest id. NaN logits never compete. The exponentials are
-// summed in pick order; lane k keeps pick k (K <= 64) and writes it.
+// summed in pick order; lane k keeps pick k (K <= 64) and writes it. The wave
+// max runs on DPP lane moves (no LDS round trips), so the winner is uniform
+// and its logit is read from the owning lane with readlane.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-constexpr int kRoutePerLane = kMaxExperts / kWave;  // 16 logits per lane
+// logits per lane: NJ = 2, 4, 8 or 16 (E <= 64 * NJ), a template parameter so
+// that the per-round scan of a lane's candidates covers only real experts
 
 // order-preserving map of a non-NaN float to uint32 (larger float -> larger key)
 __device__ __forceinline__ uint32_t ordered(float v)
@@ -28,17 +31,35 @@ __device__ __forceinline__ uint32_t ordered(float v)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// one DPP step of a wave max over 64-bit keys held as (hi, lo) words; lanes
+// without a source take key 0, which is below every candidate
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ void key_max_step(uint32_t &hi, uint32_t &lo)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
-        const uint64_t u = ((uint64_t)hi << 32) | lo;
-        v = u > v ? u : v;
-    }
-    return v;
+    const uint32_t h2 = (uint32_t)dpp_move<CTRL, ROWS>((int)hi, 0);
+    const uint32_t l2 = (uint32_t)dpp_move<CTRL, ROWS>((int)lo, 0);
+    const bool gt = h2 > hi || (h2 == hi && l2 > lo);
+    hi = gt ? h2 : hi;
+    lo = gt ? l2 : lo;
 }
 
+// largest key of the wave, in every lane (as wave_max: DPP row shifts and
+// broadcasts, the total lands in lane 63)
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    key_max_step<kRowShr + 1>(hi, lo);
+    key_max_step<kRowShr + 2>(hi, lo);
+    key_max_step<kRowShr + 4>(hi, lo);
+    key_max_step<kRowShr + 8>(hi, lo);
+    key_max_step<kRowBcast15, 0xa>(hi, lo);
+    key_max_step<kRowBcast31, 0xc>(hi, lo);
+    hi = __builtin_amdgcn_readlane(hi, kWave - 1);
+    lo = __builtin_amdgcn_readlane(lo, kWave - 1);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NJ>
 __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ logits, int T, int E,
                                                     int K, int32_t *__restrict__ ids,
                                                     float *__restrict__ w)
@@ -47,10 +68,10 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
     const float *row = logits + (size_t)t * E;
-    float v[kRoutePerLane];
+    float v[NJ];
     uint32_t avail = 0;  // bit j: logit lane + 64*j is present, not NaN, not yet picked
 #pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int e = lane + kWave * j;
         v[j] = e < E ? row[e] : 0.f;
         if (e < E && !__builtin_isnan(v[j])) avail |= 1u << j;
@@ -60,7 +81,7 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
     for (int k = 0; k < K; ++k) {
         uint64_t key = 0;  // 0: no candidate (below every real key)
 #pragma unroll
-        for (int j = 0; j < kRoutePerLane; ++j)
+        for (int j = 0; j < NJ; ++j)
             if ((avail >> j) & 1u) {
                 const uint64_t c = ((uint64_t)ordered(v[j]) << 32) |
                                    (uint32_t)(0xffffffffu - (uint32_t)(lane + kWave * j));
@@ -74,8 +95,9 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
             const int owner = id & (kWave - 1), slot = id >> 6;
             float val = 0.f;
 #pragma unroll
-            for (int j = 0; j < kRoutePerLane; ++j) val = (j == slot) ? v[j] : val;
-            val = __shfl(val, owner);
+            for (int j = 0; j < NJ; ++j) val = (j == slot) ? v[j] : val;
+            val = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, val), owner));
             if (lane == owner) avail &= ~(1u << slot);
             if (k == 0) m = val;
             e_k = expf(val - m);
@@ -95,7 +117,15 @@ __global__ __launch_bounds__(256) void k_route_topk(const float *__restrict__ lo
 hipError_t launch_route_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
                              hipStream_t s)
 {
-    hipLaunchKernelGGL(k_route_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+    const dim3 grid((T + 3) / 4), block(256);
+    if (E <= 2 * kWave)
+        hipLaunchKernelGGL(k_route_topk<2>, grid, block, 0, s, logits, T, E, K, ids, w);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(k_route_topk<4>, grid, block, 0, s, logits, T, E, K, ids, w);
+    else if (E <= 8 * kWave)
+        hipLaunchKernelGGL(k_route_topk<8>, grid, block, 0, s, logits, T, E, K, ids, w);
+    else
+        hipLaunchKernelGGL(k_route_topk<16>, grid, block, 0, s, logits, T, E, K, ids, w);
     return hipGetLastError();
 }
 

@@ -32,8 +32,11 @@ def test_route_configs(name):
     check(synth.router_logits(cfg, T), cfg.K, name)
 
 
+# E spans the kernel's logits-per-lane variants (2, 4, 8, 16 per lane) and
+# each one's first size past the previous (129, 257, 513)
 @pytest.mark.parametrize("T,E,K,seed", [(1, 1, 1, 0), (5, 3, 3, 1), (100, 64, 64, 2),
-                                        (257, 1024, 16, 3), (33, 1000, 1, 4), (2048, 512, 10, 5)])
+                                        (257, 1024, 16, 3), (33, 1000, 1, 4), (2048, 512, 10, 5),
+                                        (40, 129, 8, 6), (40, 257, 4, 8), (40, 513, 8, 9)])
 def test_route_shapes(T, E, K, seed):
     g = np.random.default_rng(seed)
     check(g.standard_normal((T, E)).astype(np.float32) * 3, K, f"seed {seed}")
