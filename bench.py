@@ -167,6 +167,9 @@ def parse():
                     help="expert weights as moe_pack_weights lays them out (packed once before "
                          "the timed steps) or row-major as generated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one captured step (a HIP graph of the step's layer "
+                         "calls) instead of eager calls; stage times stay eager")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock target of the CPU oracle sample")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -311,11 +314,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for i in range(args.steps):  # eager (also for the gate/up timer in graph mode)
         step(timer if i % TIMER_EVERY == 0 else None)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if graph is None:
+        wall = time.perf_counter() - t1
     ms = wall * 1e3 / args.steps
     st = timer.read()
     timer.close()
@@ -410,6 +428,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": d, "E": E, "top_k": K, "f": f, "tm": tm,
                    "layer_calls_per_step": ncalls,
+                   "launch": "one HIP graph replay per step" if graph is not None
+                             else "eager kernel launches",
                    "routing": {"none": "router logits N(0,1)", "normal0.5": "router logits N(0,1) "
                                "+ per-expert N(0,0.5) bias", "zipf1.1": "router logits N(0,1) + "
                                "Zipf(1.1)-ranked per-expert bias"}[cfg.bias] +
