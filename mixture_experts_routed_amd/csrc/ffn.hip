@@ -35,6 +35,13 @@
 //    feeds MFMA c, whose 16 columns are the logical columns 4*j + c of the
 //    slice. No repacking of the weights by the caller.
 //  * Loads of K-step s+S-1 are issued before the MFMAs of step s.
+//  * Packed weights (moe_pack_weights, once at load time): each wavefront's
+//    K range of a column slice is one contiguous run of 4 KB tiles already in
+//    MFMA lane order (16-byte loads, no transposes).
+//  * Big cells (packed 16-bit weights, experts with hundreds of rows, as in a
+//    long prompt planned as one call): runs of 4 items x 256 weight columns on
+//    8 wavefronts, operands loaded straight into LDS (k_big, below), which
+//    turns those experts from weight streaming into matrix-core work.
 #include "common.hpp"
 #include "launch.hpp"
 
