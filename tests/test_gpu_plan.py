@@ -76,6 +76,24 @@ FUZZ = [
 ]
 
 
+def random_plans(n=40, seed=4242):
+    """seeded random plan shapes: both plan paths, any tile, skipped and bad ids"""
+    g = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        E = int(g.choice([1, 2, 5, 31, 64, 65, 128, 300, 512, 777, 1000, 1024]))
+        K = int(g.integers(1, 17))
+        T = int(g.choice([1, 2, 7, 100, 1023, 1024, 1025, 3000, 4096, 9999, 20000, 40000]))
+        T = max(1, min(T, 200_000 // K))
+        tm = int(g.choice([1, 2, 3, 8, 16, 16, 31, 64]))
+        ps, pb = float(g.choice([0.0, 0.0, 0.1, 0.5])), float(g.choice([0.0, 0.0, 0.02]))
+        out.append((T, K, E, tm, ps, pb, 100 + k))
+    return out
+
+
+FUZZ += random_plans()
+
+
 @pytest.mark.parametrize("T,K,E,tm,ps,pb,seed", FUZZ)
 def test_plan_bit_exact_fuzz(T, K, E, tm, ps, pb, seed):
     ids = synth.random_ids(seed, T, K, E, p_skip=ps, p_bad=pb)
