@@ -102,3 +102,37 @@ def test_combine_ragged_width():
         say(f"[combine] d={d}")
         got = gpu_combine(Y, pos, T, K)
         assert np.array_equal(got.view(np.uint32), oracle.combine_f32(Y, pos, T, K).view(np.uint32))
+
+
+def random_gc(n=30, seed=5151):
+    """seeded random shapes: widths up to 8,192, top-k up to 40 (more than one
+    group of rows loaded together by the combine), tiles 1-32, skipped ids"""
+    g = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        E = int(g.choice([1, 3, 16, 64, 300, 1024]))
+        K = int(g.choice([1, 2, 7, 10, 16, 17, 33, 40]))
+        T = int(g.choice([1, 3, 64, 500, 2049]))
+        d = 8 * int(g.integers(1, 1025))
+        d = max(8, min(d, (1 << 25) // (T * K) // 8 * 8))  # expert outputs <= 128 MB
+        out.append((T, K, E, d, int(g.choice([1, 4, 16, 32])), ("f32", "f16", "bf16")[k % 3],
+                    float(g.choice([0.0, 0.2])), 200 + k))
+    return out
+
+
+@pytest.mark.parametrize("T,K,E,d,tm,dtype,ps,seed", random_gc())
+def test_gather_combine_random_shapes(T, K, E, d, tm, dtype, ps, seed):
+    ids = synth.random_ids(seed, T, K, E, p_skip=ps, p_bad=0.0)
+    w = synth.random_rows(seed, T, K)
+    g = np.random.default_rng(seed)
+    x = synth.to_dtype(g.standard_normal((T, d)).astype(np.float32), dtype)
+    p = oracle.plan(ids, w, E, tm)
+    z = abi.moe_plan_sizes(T, K, E, tm)
+    nr = len(p["stok"])
+    say(f"[gather/combine] T={T} K={K} E={E} d={d} tm={tm} {dtype}")
+    got = gpu_gather(x, dtype, p, z.max_rows)
+    ref = oracle.gather(x, p["stok"]).view(np.uint8).reshape(nr, d * synth.ELEM_BYTES[dtype])
+    assert np.array_equal(got[:nr], ref)
+    Y = g.standard_normal((max(nr, 1), d)).astype(np.float32)
+    out = gpu_combine(Y, p["pos"], T, K)
+    assert np.array_equal(out.view(np.uint32), oracle.combine_f32(Y, p["pos"], T, K).view(np.uint32))
