@@ -1204,11 +1204,15 @@ __device__ __forceinline__ int rows_of_plan(const int32_t *meta, int64_t max_row
     return (int)(nr < 0 ? 0 : (nr > max_rows ? max_rows : nr));
 }
 
+// Both reductions are instantiated per split count NS, so that the NS planes'
+// loads are issued together rather than one loop trip at a time (a split
+// layer is latency-bound); the sums stay in split order.
+
 // h[r][c..c+3] = D(silu(sum_s G_s) * sum_s U_s) for rows r < nr; pad rows
 // (stok < 0, whose partial sums are not stored) get h = 0, as unsplit
-template <typename T>
+template <typename T, int NS>
 __global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__ part,
-                                                       int64_t plane, int nsplit, int N,
+                                                       int64_t plane, int N,
                                                        const int32_t *__restrict__ stok,
                                                        const int32_t *__restrict__ meta,
                                                        int64_t max_rows, T *__restrict__ h)
@@ -1220,12 +1224,14 @@ __global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__
     if (row >= rows_of_plan(meta, max_rows)) return;
     const float *P = part + row * 2 * N + c;
     float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
-    const int ns = stok[row] < 0 ? 0 : nsplit;
-    for (int s = 0; s < ns; ++s) {
-        const float4 gv = *reinterpret_cast<const float4 *>(P + s * plane);
-        const float4 uv = *reinterpret_cast<const float4 *>(P + s * plane + N);
-        gs = make_float4(gs.x + gv.x, gs.y + gv.y, gs.z + gv.z, gs.w + gv.w);
-        us = make_float4(us.x + uv.x, us.y + uv.y, us.z + uv.z, us.w + uv.w);
+    if (stok[row] >= 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float4 gv = *reinterpret_cast<const float4 *>(P + s * plane);
+            const float4 uv = *reinterpret_cast<const float4 *>(P + s * plane + N);
+            gs = make_float4(gs.x + gv.x, gs.y + gv.y, gs.z + gv.z, gs.w + gv.w);
+            us = make_float4(us.x + uv.x, us.y + uv.y, us.z + uv.z, us.w + uv.w);
+        }
     }
     const float h0 = silu(gs.x) * us.x, h1 = silu(gs.y) * us.y;
     const float h2 = silu(gs.z) * us.z, h3 = silu(gs.w) * us.w;
@@ -1238,8 +1244,9 @@ __global__ __launch_bounds__(256) void k_reduce_gateup(const float *__restrict__
 }
 
 // y[r][c..c+3] = sw[r] * sum_s Y_s for rows r < nr with stok[r] >= 0
+template <int NS>
 __global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ part, int64_t plane,
-                                                     int nsplit, int N,
+                                                     int N,
                                                      const int32_t *__restrict__ stok,
                                                      const float *__restrict__ sw,
                                                      const int32_t *__restrict__ meta,
@@ -1252,7 +1259,8 @@ __global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ p
     if (row >= rows_of_plan(meta, max_rows) || stok[row] < 0) return;
     const float *P = part + row * N + c;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nsplit; ++s) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
         const float4 v = *reinterpret_cast<const float4 *>(P + s * plane);
         a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
     }
@@ -1262,6 +1270,39 @@ __global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ p
 }
 
 // ---- host launchers --------------------------------------------------------
+// the reductions' launch for a split count in [2, kMaxSplit] (any other count
+// is refused)
+template <typename T, int NS = 2>
+hipError_t reduce_gateup(int nsplit, dim3 grid, hipStream_t s, const float *part, int64_t plane, int N,
+                   const int32_t *stok, const int32_t *meta, int64_t max_rows, T *h)
+{
+    if constexpr (NS <= kMaxSplit) {
+        if (nsplit != NS)
+            return reduce_gateup<T, NS + 1>(nsplit, grid, s, part, plane, N, stok, meta, max_rows,
+                                            h);
+        hipLaunchKernelGGL((k_reduce_gateup<T, NS>), grid, dim3(256), 0, s, part, plane, N, stok,
+                           meta, max_rows, h);
+        return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int NS = 2>
+hipError_t reduce_down(int nsplit, dim3 grid, hipStream_t s, const float *part, int64_t plane, int N,
+                 const int32_t *stok, const float *sw, const int32_t *meta, int64_t max_rows,
+                 float *y)
+{
+    if constexpr (NS <= kMaxSplit) {
+        if (nsplit != NS)
+            return reduce_down<NS + 1>(nsplit, grid, s, part, plane, N, stok, sw, meta, max_rows,
+                                       y);
+        hipLaunchKernelGGL((k_reduce_down<NS>), grid, dim3(256), 0, s, part, plane, N, stok, sw,
+                           meta, max_rows, y);
+        return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, bool runs_first, hipStream_t s)
 {
@@ -1326,10 +1367,12 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     else
         hipLaunchKernelGGL((k_expert_gemm<T, true, false, PACKED>), grid, dim3(256), 0, s, p,
                            ctl_of(scratch), items_of(scratch));
-    if (z.split_gu > 1)
-        hipLaunchKernelGGL(k_reduce_gateup<T>, dim3(reduce_blocks(z.max_rows, f)), dim3(256), 0, s,
-                           p.part, p.plane, p.nsplit, f, stok, meta, z.max_rows,
-                           static_cast<T *>(h));
+    if (z.split_gu > 1) {
+        const hipError_t e = reduce_gateup<T>(p.nsplit, dim3(reduce_blocks(z.max_rows, f)), s,
+                                              p.part, p.plane, f, stok, meta, z.max_rows,
+                                              static_cast<T *>(h));
+        if (e != hipSuccess) return e;
+    }
     return hipGetLastError();
 }
 
@@ -1355,9 +1398,11 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
     }
     hipLaunchKernelGGL((k_expert_gemm<T, false, false, PACKED>), dim3((unsigned)z.blocks_dn),
                        dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch));
-    if (z.split_dn > 1)
-        hipLaunchKernelGGL(k_reduce_down, dim3(reduce_blocks(z.max_rows, d)), dim3(256), 0, s,
-                           p.part, p.plane, p.nsplit, d, stok, sw, meta, z.max_rows, y);
+    if (z.split_dn > 1) {
+        const hipError_t e = reduce_down(p.nsplit, dim3(reduce_blocks(z.max_rows, d)), s, p.part,
+                                         p.plane, d, stok, sw, meta, z.max_rows, y);
+        if (e != hipSuccess) return e;
+    }
     return hipGetLastError();
 }
 
