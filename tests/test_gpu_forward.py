@@ -71,6 +71,36 @@ def test_forward_small_all_tokens(cfg):
     compare(case, case.ids, case.w, case.x, got, np.arange(cfg.T, dtype=np.int32))
 
 
+def split_cases():
+    """one small layer per (dtype, projection, split count 2..8): the K range
+    of the split projection is 8 steps per split (32 K-values per step for
+    16-bit types, 16 for fp32), the other projection too short to split"""
+    out = []
+    for dtype, kstep in (("f32", 16), ("f16", 32), ("bf16", 32)):
+        for ns in range(2, 9):
+            kd = 8 * kstep * ns
+            out.append((custom(f"split_gateup_{ns}_{dtype}", T=8, d=kd, E=4, K=2, f=64,
+                               dtype=dtype, x_std=1.0, seed=700 + ns), (ns, 1)))
+            out.append((custom(f"split_down_{ns}_{dtype}", T=8, d=64, E=4, K=2, f=kd,
+                               dtype=dtype, x_std=1.0, seed=800 + ns), (1, ns)))
+    return out
+
+
+SPLITS = split_cases()
+
+
+@pytest.mark.parametrize("cfg,splits", SPLITS, ids=[c[0].name for c in SPLITS])
+def test_forward_every_split_count(cfg, splits):
+    """each split count's reduction (gate/up per dtype, down) against the oracle"""
+    z = abi.moe_plan_sizes(cfg.T, cfg.K, cfg.E, cfg.tm)
+    assert abi.moe_ffn_splits(cfg.E, cfg.d, cfg.f, cfg.tm, z.max_rows,
+                              abi.DTYPE_NAME[cfg.dtype]) == splits
+    case = make_case(cfg)
+    say(f"[forward] {cfg.name}")
+    got, _ = gpu_forward(case, case.ids, case.w, case.x)
+    compare(case, case.ids, case.w, case.x, got, np.arange(cfg.T, dtype=np.int32))
+
+
 def sample_tokens(T, seed, n=24):
     g = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, T - 1], g.choice(T, min(n, T), replace=False)])).astype(
