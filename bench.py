@@ -47,6 +47,56 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "libbench_probe.so")
+
+
+def build_probe() -> str:
+    """Compile the benchmark's streaming-read probe (bench_probe.hip) for gfx950 into
+    libbench_probe.so beside this file. It is a measurement helper of the benchmark,
+    not part of the layer's library."""
+    import subprocess
+
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-o", PROBE_LIB + ".tmp", PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("bench probe build failed:\n" + r.stdout + r.stderr)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
+_probe = None
+
+
+def probe_lib():
+    """The probe library (built by build_probe(); raises if missing)."""
+    import ctypes
+
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB):
+            raise FileNotFoundError(f"{PROBE_LIB} is missing: run bench.build_probe()")
+        L = ctypes.CDLL(PROBE_LIB)
+        L.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+        L.bench_stream_read.restype = ctypes.c_int
+        _probe = L
+    return _probe
+
+
+def stream_read(src, sink, stream=None):
+    """One streaming read of the GPU tensor `src` by the probe (on torch's current stream)."""
+    import torch
+
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = probe_lib().bench_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                       sink.data_ptr(), sink.numel(), s)
+    if rc != 0:
+        raise RuntimeError(f"bench_stream_read: status {rc}")
+
+
 def gemm_source_hash() -> str:
     import hashlib
 
@@ -366,17 +416,17 @@ def main():
 
     step_us = {"warm": distribution(False), "cold": distribution(True), "samples": ndist}
 
-    # the library's streaming-read probe over 2 GiB (16-byte non-temporal loads,
+    # the benchmark's streaming-read probe over 2 GiB (16-byte non-temporal loads,
     # the weight streams' access pattern): the read rate this box attains
     del flush
     src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     sink = torch.zeros(8192, dtype=torch.int32, device=dev)
     for _ in range(2):
-        abi.moe_stream_read(src, sink)
+        stream_read(src, sink)
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
     for _ in range(10):
-        abi.moe_stream_read(src, sink)
+        stream_read(src, sink)
     c1.record()
     torch.cuda.synchronize()
     read_gbs = 10 * src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
@@ -453,7 +503,7 @@ def main():
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
         "stages_tflops": {k: round(v / (us[k] * 1e6), 1) for k, v in flops.items() if us.get(k)},
         "roofline": dict(roof, read_probe_gbs=round(read_gbs, 1),
-                         read_probe_note="same run: moe_stream_read over 2 GiB (each workgroup "
+                         read_probe_note="same run: the benchmark read probe (bench_probe.hip) over 2 GiB (each workgroup "
                                          "one contiguous chunk, 16-byte non-temporal loads, "
                                          "no compute) reaches this rate"),
     }

@@ -1,17 +1,20 @@
-// Streaming-read probe (measurement only, not part of the layer): reads a
-// device buffer once with 16-byte non-temporal loads, the access pattern of the
-// grouped GEMMs' weight streams, so that a benchmark can quote in the same run
-// the read rate the GPU attains next to the layer's kernels.
+// Streaming-read probe of the benchmark (measurement only; not part of the
+// layer's library or its C ABI): reads a device buffer once with 16-byte
+// non-temporal loads, the access pattern of the grouped GEMMs' weight streams,
+// so that the benchmark can quote in the same run the read rate the GPU
+// attains next to the layer's kernels. Built by bench.build_probe() into
+// libbench_probe.so beside bench.py.
 //
 // Each workgroup streams one contiguous chunk: 256 threads x 16 bytes = 4 KB
 // per row, 8 rows in flight per thread. (Measured on MI355X: this reaches
 // 7.0-7.1 TB/s; a grid-stride walk over the whole buffer stays near 6 TB/s.)
 // Every loaded word feeds an XOR that decides a store, so no load can be
 // removed.
-#include "common.hpp"
-#include "launch.hpp"
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
 
-namespace moe {
+namespace {
 
 constexpr int kProbeThreads = 256;
 constexpr int kProbeUnroll = 8;
@@ -44,14 +47,23 @@ __global__ __launch_bounds__(kProbeThreads) void k_stream_read(const uint4 *__re
     if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
-hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
-                              hipStream_t s)
+}  // namespace
+
+// One streaming read of src (bytes / 16 16-byte words) on `stream`. sink
+// [sink_words] receives at most one word per workgroup, and only for one
+// checksum value in 2^32; its contents carry no meaning. Returns 0, 1 for a
+// bad argument (misaligned src or sink, bytes < 16, sink_words < 1), 3 when
+// the launch fails.
+extern "C" int bench_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
+                                 void *stream)
 {
+    if (!src || !sink || reinterpret_cast<uintptr_t>(src) % 16 ||
+        reinterpret_cast<uintptr_t>(sink) % 4 || bytes < 16 || sink_words < 1)
+        return 1;
     // 32 workgroups per CU on 256 CUs, capped by the sink (one word per workgroup)
     const int blocks = sink_words < 8192 ? sink_words : 8192;
-    hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(kProbeThreads), 0, s,
-                       static_cast<const uint4 *>(src), bytes / 16, sink);
-    return hipGetLastError();
+    hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(kProbeThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint4 *>(src),
+                       bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 3;
 }
-
-}  // namespace moe

@@ -357,20 +357,6 @@ int moe_forward_timed(const void *x, const int32_t *ids, const float *w, const v
                       int f, int tm, void *workspace, size_t ws_bytes, float *out,
                       moe_stream_t stream, moe_timer_t *timer);
 
-/*
- * moe_stream_read -- measurement only, not a step of the layer: one streaming
- * read of src (bytes / 16 16-byte words, non-temporal loads, each workgroup
- * one contiguous chunk), so that a benchmark can quote the read rate the GPU
- * attains beside the layer's kernels. sink
- * [sink_words] (device) receives at most one word per workgroup, and only for
- * one checksum value in 2^32 (the store keeps the loads live); its contents
- * carry no meaning. Enqueued on `stream`.
- * Errors: MOE_EINVAL for misaligned src (16 B) or sink (4 B), bytes < 16,
- * sink_words < 1; MOE_EHIP on a failed launch.
- */
-int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
-                    moe_stream_t stream);
-
 /* moe_forward_packed with an event pair recorded around every kernel into
  * `timer` (NULL: identical to moe_forward_packed). */
 int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,

@@ -68,7 +68,6 @@ _SIGS = {
     "moe_timer_create": [ctypes.POINTER(P), I32, ctypes.c_uint],
     "moe_timer_destroy": [P],
     "moe_timer_read": [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
-    "moe_stream_read": [P, SZ, P, I32, P],
     "moe_packed_weight_bytes": [I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
     "moe_pack_weights": [P, I32, I32, I32, I32, I32, P, SZ, P],
     "moe_expert_ffn_packed": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ,
@@ -164,13 +163,6 @@ def moe_forward_layout(T, K, E, d, f, tm, dtype: int) -> ForwardLayout:
     L = ForwardLayout()
     _check("moe_forward_layout", lib().moe_forward_layout(T, K, E, d, f, tm, dtype, ctypes.byref(L)))
     return L
-
-
-def moe_stream_read(src, sink, stream=None):
-    """Measurement only: one streaming read of the GPU tensor `src` (see the header)."""
-    nbytes = src.numel() * src.element_size()
-    _check("moe_stream_read", lib().moe_stream_read(_dev(src, "src"), nbytes, _dev(sink, "sink"),
-                                                    sink.numel(), _stream(stream)))
 
 
 def moe_status_str(status: int) -> str:

@@ -426,15 +426,6 @@ int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int
     return combine_impl(y, max_rows, pos, T, K, d, out, as_stream(stream), nullptr);
 }
 
-int moe_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
-                    moe_stream_t stream)
-{
-    if (!aligned(src, 16) || !aligned(sink, 4) || bytes < 16 || sink_words < 1) return MOE_EINVAL;
-    if (moe::launch_stream_read(src, bytes, sink, sink_words, as_stream(stream)) != hipSuccess)
-        return MOE_EHIP;
-    return MOE_OK;
-}
-
 int moe_forward_layout(int T, int K, int E, int d, int f, int tm, int dtype,
                        moe_forward_layout_t *out)
 {

@@ -83,10 +83,4 @@ size_t packed_weight_bytes(int E, int Kd, int N, bool gateup, int dtype);
 hipError_t launch_pack(int dtype, const void *src, int E, int Kd, int N, bool gateup, void *dst,
                        hipStream_t s);
 
-// ---- measurement only ----
-// one streaming read of `bytes` (16-byte words) of src; sink holds sink_words
-// words, one per workgroup (written only for one checksum value in 2^32)
-hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
-                              hipStream_t s);
-
 }  // namespace moe

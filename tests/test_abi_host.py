@@ -117,14 +117,6 @@ def test_packed_weight_sizes_and_rejects():
     assert L.moe_pack_weights(A + 8, 1, 3, 328, 200, 0, A, 1 << 30, None) == 1  # misaligned
 
 
-def test_stream_read_rejects_bad_arguments():
-    L = abi.lib()
-    assert L.moe_stream_read(A + 8, 1 << 20, A, 16, None) == 1   # src not 16-byte aligned
-    assert L.moe_stream_read(A, 8, A, 16, None) == 1             # fewer than 16 bytes
-    assert L.moe_stream_read(A, 1 << 20, A, 0, None) == 1        # no sink
-    assert L.moe_stream_read(None, 1 << 20, A, 16, None) == 1
-
-
 def test_forward_layout_is_consistent():
     L = abi.moe_forward_layout(2048, 10, 512, 2560, 768, 16, abi.MOE_F16)
     z = abi.moe_plan_sizes(2048, 10, 512, 16)

@@ -111,3 +111,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
     assert r.stdout.strip() == ""  # no bench line
+
+
+def test_read_probe_is_outside_the_layer_library_and_rejects_bad_arguments():
+    """the benchmark's read probe lives in its own library beside bench.py: the
+    layer's library exports no probe, and the probe refuses bad arguments before
+    any HIP call (status 1)"""
+    import ctypes
+
+    from mixture_experts_routed_amd import abi
+
+    assert not hasattr(abi.lib(), "moe_stream_read")
+    assert "stream_read" not in open(os.path.join(ROOT, "include", "moe_routed.h")).read()
+    L = bench.probe_lib()
+    A = 1 << 20  # a made-up, never dereferenced address
+    assert L.bench_stream_read(A + 8, 1 << 20, A, 16, None) == 1  # src not 16-byte aligned
+    assert L.bench_stream_read(A, 8, A, 16, None) == 1            # fewer than 16 bytes
+    assert L.bench_stream_read(A, 1 << 20, A, 0, None) == 1       # no sink
+    assert L.bench_stream_read(None, 1 << 20, A, 16, None) == 1
+    assert L.bench_stream_read(A, 1 << 20, A + 2, 16, None) == 1  # sink not 4-byte aligned
+    del ctypes
