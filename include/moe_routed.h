@@ -66,7 +66,13 @@ typedef void *moe_stream_t; /* hipStream_t */
 
 enum moe_dtype { MOE_F32 = 0, MOE_F16 = 1, MOE_BF16 = 2 };
 
-enum moe_status { MOE_OK = 0, MOE_EINVAL = 1, MOE_EUNSUPPORTED = 2, MOE_EHIP = 3 };
+enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,
+    MOE_EUNSUPPORTED = 2,
+    MOE_EHIP = 3,
+    MOE_ENOSPACE = 4 /* larger than the fixed buffer of moe_forward_packed_noalloc */
+};
 
 /* Fields of the device array meta[MOE_META_N] written by moe_plan. */
 enum moe_meta_field {
@@ -364,6 +370,37 @@ int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,
                              int dtype, int T, int K, int E, int d, int f, int tm,
                              void *workspace, size_t ws_bytes, float *out, moe_stream_t stream,
                              moe_timer_t *timer);
+
+/*
+ * moe_forward_packed_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_forward_packed with its workspace taken from a fixed buffer
+ * inside this library instead of a caller argument. The caller still passes
+ * the inputs and `out`, as for moe_forward_packed; results are the same bits.
+ *  - The buffer is MOE_NOALLOC_WORKSPACE_BYTES of device memory per GPU,
+ *    reserved when the library's code is loaded on that GPU and held until the
+ *    process ends. It covers decode-sized batches (e.g. 4 tokens, hidden 2816,
+ *    128 experts, top-8, intermediate 704 needs 22.7 MiB).
+ *  - A request whose moe_forward_workspace() exceeds the buffer returns
+ *    MOE_ENOSPACE before any HIP call.
+ *  - The first call on each device looks up that device's buffer address
+ *    (hipGetSymbolAddress); make that first call outside graph capture. Later
+ *    calls allocate nothing, clear nothing with memset and never wait on the
+ *    host, so they can be captured.
+ *  - `stream` must belong to the current device (MOE_EINVAL otherwise); NULL
+ *    is the current device's default stream.
+ *  - All calls on one GPU share that GPU's buffer, which keeps the last call's
+ *    contents (nothing in it needs to start at zero): calls that can overlap on
+ *    one GPU (different streams or threads without ordering between them) race
+ *    on it and must be serialised by the caller.
+ * Errors: those of moe_forward_packed, plus MOE_ENOSPACE, and
+ * MOE_EUNSUPPORTED for a device ordinal of 64 or more.
+ */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+int moe_forward_packed_noalloc(const void *x, const int32_t *ids, const float *w,
+                               const void *pw_gate, const void *pw_up, const void *pw_down,
+                               int dtype, int T, int K, int E, int d, int f, int tm, float *out,
+                               moe_stream_t stream);
 
 /* Static description of a status code. */
 const char *moe_status_str(int status);

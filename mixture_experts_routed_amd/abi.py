@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
 
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
 MOE_W_GATE_UP, MOE_W_DOWN = 0, 1
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error",
+          4: "larger than the allocation-free call's fixed buffer"}
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # MOE_NOALLOC_WORKSPACE_BYTES
 META_FIELDS = ("nent", "nblk", "nr", "nt", "nactive", "maxcnt", "nskip", "nbad", "tm", "E", "K")
 META_N = 11
 STAGES = ("hist", "scan", "place", "gather", "worklist", "gateup", "down", "combine")
@@ -75,6 +77,7 @@ _SIGS = {
     "moe_forward_packed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P],
     "moe_forward_packed_timed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P,
                                  P],
+    "moe_forward_packed_noalloc": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, P],
 }
 
 EXPORTS = tuple(_SIGS) + ("moe_status_str",)
@@ -255,6 +258,15 @@ def moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, works
         _check(name, getattr(lib(), name)(*args))
     else:
         _check(name + "_timed", getattr(lib(), name + "_timed")(*args, timer.handle))
+
+
+def moe_forward_packed_noalloc(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, E, d, f, tm, out,
+                               stream=None):
+    """moe_forward_packed with the library's fixed workspace (no workspace argument)."""
+    _check("moe_forward_packed_noalloc", lib().moe_forward_packed_noalloc(
+        _dev(x, "x"), _dev(ids, "ids"), _dev(w, "w"), _dev(pw_gate, "pw_gate"),
+        _dev(pw_up, "pw_up"), _dev(pw_down, "pw_down"), dtype, T, K, E, d, f, tm,
+        _dev(out, "out"), _stream(stream)))
 
 
 class Timer:

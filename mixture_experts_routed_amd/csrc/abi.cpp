@@ -531,6 +531,7 @@ const char *moe_status_str(int status)
     case MOE_EINVAL: return "invalid argument";
     case MOE_EUNSUPPORTED: return "unsupported by this build";
     case MOE_EHIP: return "HIP runtime error";
+    case MOE_ENOSPACE: return "request larger than the fixed buffer of the allocation-free call";
     default: return "unknown status";
     }
 }

@@ -157,3 +157,23 @@ def test_route_rejects_bad_arguments():
     assert L.moe_route_topk(A, 4, 2048, 8, A, A, None) == 2   # E too large
     assert L.moe_route_topk(A, 4, 512, 65, A, A, None) == 2   # K too large
     assert L.moe_route_topk(A + 2, 4, 8, 2, A, A, None) == 1  # misaligned
+
+
+def test_noalloc_refuses_requests_beyond_its_buffer_before_any_hip_call():
+    """the allocation-free forward has a fixed buffer of MOE_NOALLOC_WORKSPACE_BYTES:
+    a larger request (the prefill shape needs ~454 MiB) is refused with
+    MOE_ENOSPACE (4) on the host, like the other argument checks"""
+    L = abi.lib()
+    assert abi.NOALLOC_WORKSPACE_BYTES == 64 << 20
+    assert "MOE_NOALLOC_WORKSPACE_BYTES (64u * 1024u * 1024u)" in open(HEADER).read()
+    A = 1 << 20  # never dereferenced
+    need = abi.moe_forward_workspace(2048, 10, 512, 2560, 768, 16, abi.MOE_F16)
+    assert need > abi.NOALLOC_WORKSPACE_BYTES
+    assert L.moe_forward_packed_noalloc(A, A, A, A, A, A, abi.MOE_F16, 2048, 10, 512, 2560, 768,
+                                        16, A, None) == 4
+    # bad sizes keep their own status
+    assert L.moe_forward_packed_noalloc(A, A, A, A, A, A, abi.MOE_F16, 0, 10, 512, 2560, 768, 16,
+                                        A, None) == 1
+    assert L.moe_forward_packed_noalloc(A, A, A, A, A, A, abi.MOE_F16, 4, 8, 2000, 2816, 704, 16,
+                                        A, None) == 2
+    assert abi.moe_status_str(4).startswith("request larger than the fixed buffer")
