@@ -1,6 +1,6 @@
 """GPU parity of moe_expert_ffn alone, fed the oracle's plan and gathered rows:
-the SwiGLU output h and the weighted expert output y of every (sampled) entry
-against the oracle's per-entry loop, max|d|/max|ref| within the tolerance of
+the SwiGLU output h and the weighted expert output y of every entry (a large
+sample at the 32K-token one-call shape) against the oracle's per-entry loop, max|d|/max|ref| within the tolerance of
 the element type (1e-5 fp32, 5e-3 fp16/bf16). Pad rows of y stay untouched.
 Shapes are chosen to take every launch path: K split into ranges (few work
 items) in either projection, and runs of 2 or 4 work items of one expert that
@@ -83,20 +83,24 @@ def test_ffn_small_all_entries(cfg):
 
 
 @pytest.mark.parametrize("name", synth.CONFIG_ORDER)
-def test_ffn_configs_sampled(name):
+def test_ffn_configs_every_entry(name):
+    """h and y of every entry of the workload's first layer call against the
+    oracle; the long prompt planned as one call (327,680 entries) compares 8,192:
+    its first and last, every 16th of the heaviest expert's and a seeded sample"""
     cfg = synth.CONFIGS[name]
     case = make_case(cfg)
     Tc = cfg.tokens_per_call
     ids, w, x = case.ids[:Tc], case.w[:Tc], case.x[:Tc]
     flat = ids.reshape(-1)
     valid = np.nonzero((flat >= 0) & (flat < cfg.E))[0]
-    g = np.random.default_rng(cfg.seed)
-    n = min(len(valid), 96)
-    ent = np.unique(np.concatenate([valid[:4], valid[-4:], g.choice(valid, n, replace=False)]))
-    if cfg.bias == "zipf1.1":  # include entries of the heaviest expert (several work items)
+    ent = valid
+    if len(valid) > 32768:
+        g = np.random.default_rng(cfg.seed)
         top = np.bincount(flat[valid], minlength=cfg.E).argmax()
         heavy = valid[flat[valid] == top]
-        ent = np.unique(np.concatenate([ent, heavy[:: max(1, len(heavy) // 24)]]))
+        ent = np.unique(np.concatenate([valid[:64], valid[-64:], heavy[::16]]))
+        ent = np.unique(np.concatenate([ent, g.choice(valid, 8192 - len(ent), replace=False)]))
+    say(f"[ffn] {name}: {len(ent)} of {len(valid)} entries")
     run_ffn(case, ids, w, x, ent.astype(np.int32))
     case.drop_device()
 

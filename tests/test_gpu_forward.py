@@ -1,9 +1,11 @@
 """GPU parity of moe_forward (the whole layer, the launch configuration the
 benchmark times) against the oracle's naive per-(token, expert) loop, with the
 SwiGLU output rounded like the GPU's operand (REF-R) and exact (REF-X):
-max|d|/max|ref| <= 1e-5 for fp32 inputs, <= 5e-3 for fp16/bf16. Full size
-configs compare a seeded sample of tokens; the long prompt runs all 16 chunks.
-Also: bitwise run-to-run determinism and the degenerate cases."""
+max|d|/max|ref| <= 1e-5 for fp32 inputs, <= 5e-3 for fp16/bf16. Full-size
+workloads compare every token against REF-R, with row-major and with packed
+weights (the benchmark's layout), and a seeded sample of 256 tokens against
+REF-X; the long prompt runs all 16 chunks. Also: bitwise run-to-run
+determinism and the degenerate cases."""
 import numpy as np
 import pytest
 import torch
@@ -107,37 +109,90 @@ def sample_tokens(T, seed, n=24):
         np.int32)
 
 
+_REF = {}
+
+
+def ref_all_tokens(case):
+    """REF-R of every token of a workload, from the oracle's per-token loop, in
+    pieces of 4096 tokens (progress shows between them). A token's output does not
+    depend on how the tokens are cut into layer calls, so the long prompt's chunked
+    and one-call forms (same seed and inputs) share one reference."""
+    cfg = case.cfg
+    key = (cfg.seed, cfg.T, cfg.d, cfg.E, cfg.K, cfg.f, cfg.dtype, cfg.bias, cfg.tail_skip,
+           cfg.x_std, cfg.w_std)
+    if key not in _REF:
+        ref = np.empty((cfg.T, cfg.d), np.float32)
+        for t0 in range(0, cfg.T, 4096):
+            tok = np.arange(t0, min(cfg.T, t0 + 4096), dtype=np.int32)
+            ref[tok] = oracle.ffn(case.x, case.ids, case.w, case.wg, case.wu, case.wd, cfg.dtype,
+                                  True, tokens=tok)
+            say(f"  oracle REF-R: tokens {t0}..{tok[-1]} of {cfg.T}")
+        _REF.clear()  # one workload's reference at a time (the long prompt's is 335 MB)
+        _REF[key] = ref
+    return _REF[key]
+
+
+def compare_all(case, ids, w, x, got, t0, ref_r, nx=256, seed=0):
+    """every token against REF-R (got[i] is token t0 + i), and a seeded sample of nx
+    tokens (all of them when fewer) against REF-X"""
+    cfg = case.cfg
+    T = got.shape[0]
+    err = rel_err(got, ref_r[t0:t0 + T])
+    say(f"  REF-R all {T} tokens: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
+    toks = (np.arange(T, dtype=np.int32) if T <= nx else
+            np.sort(np.random.default_rng(seed).choice(T, nx, replace=False)).astype(np.int32))
+    ref_x = oracle.ffn(x, ids, w, case.wg, case.wu, case.wd, cfg.dtype, False, tokens=toks)
+    err = rel_err(got[toks], ref_x.astype(np.float32))
+    say(f"  REF-X {len(toks)} tokens: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
+
+
 @pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16",
                                   "prefill_tailskip_fp16", "long_onepass_fp16"])
-def test_forward_full_size_sampled(name):
+def test_forward_full_size_every_token(name):
+    """row-major weights (moe_forward) and packed weights (moe_forward_packed, as
+    the benchmark runs the layer): every token's output against the oracle"""
     cfg = synth.CONFIGS[name]
     case = make_case(cfg)
-    say(f"[forward] {name} full size")
-    got, _ = gpu_forward(case, case.ids, case.w, case.x)
-    toks = sample_tokens(cfg.T, cfg.seed)
-    if cfg.bias == "zipf1.1":  # tokens of the heaviest expert (hundreds of work items)
-        top = np.bincount(case.ids[case.ids >= 0], minlength=cfg.E).argmax()
-        hot = np.nonzero((case.ids == top).any(axis=1))[0]
-        toks = np.unique(np.concatenate([toks, hot[:: max(1, len(hot) // 8)]])).astype(np.int32)
-    compare(case, case.ids, case.w, case.x, got, toks)
+    ref_r = ref_all_tokens(case)
+    pk = abi.pack(case.d("wg"), case.d("wu"), case.d("wd"))
+    x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
+    ws = None
+    for packed in (None, pk):
+        say(f"[forward] {name} full size, {'packed' if packed else 'row-major'} weights")
+        out, ws = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                              workspace=ws, packed=packed)
+        torch.cuda.synchronize()
+        compare_all(case, case.ids, case.w, case.x, host(out), 0, ref_r, seed=cfg.seed)
+    del pk, out, ws
     case.drop_device()
 
 
-def test_forward_long_prompt_all_chunks():
+def test_forward_long_prompt_all_chunks_every_token():
+    """the long prompt as 16 layer calls of 2,048 tokens (packed weights, as the
+    benchmark runs it; row-major on the first, last and most skewed chunk):
+    every token of every chunk against REF-R, 64 tokens per chunk against REF-X"""
     cfg = synth.CONFIGS["long_skewed_fp16"]
     case = make_case(cfg)
+    ref_r = ref_all_tokens(case)
+    pk = abi.pack(case.d("wg"), case.d("wu"), case.d("wd"))
+    Tc = cfg.tokens_per_call
+    top_rows = [np.bincount(chunk_of(case, c)[0].reshape(-1), minlength=cfg.E).max()
+                for c in range(cfg.ncalls)]
+    skewed = int(np.argmax(top_rows))
     ws = None
     for c in range(cfg.ncalls):
         ids, w, x = chunk_of(case, c)
-        say(f"[forward] long_skewed_fp16 chunk {c}")
-        got, ws = gpu_forward(case, ids, w, x, ws)
-        toks = sample_tokens(cfg.tokens_per_call, cfg.seed + c, n=6)
-        # also tokens routed to the chunk's heaviest expert
-        flat = ids.reshape(-1)
-        top = np.bincount(flat, minlength=cfg.E).argmax()
-        hot = np.nonzero((ids == top).any(axis=1))[0]
-        toks = np.unique(np.concatenate([toks, hot[:: max(1, len(hot) // 4)]])).astype(np.int32)
-        compare(case, ids, w, x, got, toks)
+        for packed in ((pk, None) if c in (0, cfg.ncalls - 1, skewed) else (pk,)):
+            say(f"[forward] long_skewed_fp16 chunk {c} (top expert {top_rows[c]} rows), "
+                f"{'packed' if packed else 'row-major'}")
+            out, ws = abi.forward(dev(x, cfg.dtype), dev(ids), dev(w), case.d("wg"),
+                                  case.d("wu"), case.d("wd"), tm=cfg.tm, workspace=ws,
+                                  packed=packed)
+            torch.cuda.synchronize()
+            compare_all(case, ids, w, x, host(out), c * Tc, ref_r, nx=64, seed=cfg.seed + c)
+    del pk, out, ws
     case.drop_device()
 
 
