@@ -17,7 +17,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
+# a different build of the same sources may be named here (the tests load a
+# build whose host code carries AddressSanitizer this way)
+LIB_PATH = os.environ.get("MOE_ROUTED_LIB_OVERRIDE") or os.path.join(HERE, "libmoe_routed.so")
 
 MOE_F32, MOE_F16, MOE_BF16 = 0, 1, 2
 MOE_W_GATE_UP, MOE_W_DOWN = 0, 1

@@ -49,21 +49,25 @@ def _run(cmd, verbose):
         print(msg)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, host_flags=(), lib: str = LIB, build_dir: str = BUILD) -> str:
+    """Build the library at `lib`. host_flags are added to the host compilation only
+    (each passed behind -Xarch_host), e.g. the tests' AddressSanitizer build of the
+    host code; the device code is the same either way."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
+    xhost = [a for f in host_flags for a in ("-Xarch_host", f)]
     objs = []
     cmds = []
     for s in SOURCES:
-        o = os.path.join(BUILD, s.replace(".", "_") + ".o")
+        o = os.path.join(build_dir, s.replace(".", "_") + ".o")
         objs.append(o)
-        cmds.append([cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        cmds.append([cc, *FLAGS, *xhost, "-c", os.path.join(CSRC, s), "-o", o])
     with ThreadPoolExecutor(len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *xhost, "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
