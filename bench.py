@@ -207,6 +207,23 @@ def recorded_traffic(kernel: str):
     return None
 
 
+def timed_us(fn, n):
+    """mean microseconds per call of fn() over n back-to-back calls after 3 warm-up
+    calls, from torch events on the current stream (the stream the library's calls
+    are enqueued on)"""
+    import torch
+
+    for _ in range(3):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +277,36 @@ def stage_bytes(cfg, meta, T):
         # combine: y rows of every entry read, out written, pos read
         "combine": nreal * cfg.d * 4 + T * cfg.d * 4 + nent * 4,
     }
+
+
+def plan_bytes(cfg, meta):
+    """Algorithmic bytes of the routing plan: ids read twice (histogram and placement),
+    router weights read, pos written, stok and sw written on every row (pads included),
+    the per-block offsets boff written, cnt and eoff written, one tile id per tm rows."""
+    nent, nblk, nr, nt = int(meta[0]), int(meta[1]), int(meta[2]), int(meta[3])
+    return 2 * nent * 4 + nent * 4 + nent * 4 + nr * 8 + nblk * cfg.E * 4 + 2 * cfg.E * 4 + nt * 4
+
+
+def gather_bytes(cfg, meta, T):
+    """Algorithmic bytes of the standalone gather: each token's row read once, every
+    expert-sorted row written (pad rows as zeros)."""
+    es = 2 if cfg.dtype != "f32" else 4
+    return T * cfg.d * es + int(meta[2]) * cfg.d * es
+
+
+def plan_gather_combine(cfg, meta, T, plan_us, gather_us, combine_us):
+    """The plan, gather and combine together against the HBM peak (the layer's
+    memory-bound steps other than the grouped GEMMs), with the 60% bar."""
+    b = plan_bytes(cfg, meta) + gather_bytes(cfg, meta, T) + stage_bytes(cfg, meta, T)["combine"]
+    us = plan_us + gather_us + combine_us
+    gbs = b / (us * 1e3)
+    return {"bytes": b, "us": {"plan": round(plan_us, 2), "gather": round(gather_us, 2),
+                               "combine": round(combine_us, 2), "total": round(us, 2)},
+            "gbs": round(gbs, 1), "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 3),
+            "bar": 0.6, "meets_bar": gbs / HBM_PEAK_GBS >= 0.6,
+            "note": "gather timed standalone (moe_gather on the same plan); moe_forward itself "
+                    "fuses the gather into the gate/up operand loads, so its step has no gather "
+                    "launch"}
 
 
 def cpu_baseline(cfg, ids, w, x, seconds):
@@ -449,6 +496,58 @@ def main():
 
     L = abi.moe_forward_layout(T, K, E, d, f, tm, abi.DTYPE_NAME[cfg.dtype])
     meta = ws[L.meta: L.meta + 4 * abi.META_N].view(torch.int32).cpu().numpy()
+
+    # the standalone gather (moe_gather) on the last call's plan, into the workspace's
+    # xs rows (which moe_forward leaves unused when it fuses the gather)
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    R = abi.moe_plan_sizes(T, K, E, tm).max_rows
+    stok_d = ws[L.stok: L.stok + 4 * R].view(torch.int32)
+    meta_d = ws[L.meta: L.meta + 4 * abi.META_N].view(torch.int32)
+    xs_d = ws[L.xs: L.xs + R * d * tdt.itemsize]
+    cx = chunks[-1][0]
+
+    def gather():
+        abi.moe_gather(cx, dt, T, d, stok_d, meta_d, R, xs_d)
+
+    gather_us = timed_us(gather, args.steps)
+
+    # the plan alone at the four sizes of the page's plan table (512 experts, top-10,
+    # tm 16, this workload's routing): moe_plan into its own buffers
+    plan_sizes = {}
+    if (E, K, tm) == (512, 10, 16):
+        for Tp in (128, 512, 1024, 2048):
+            pid, pw = synth.routing(cfg, Tp)
+            pid, pw = torch.from_numpy(pid).to(dev), torch.from_numpy(pw).to(dev)
+            o = abi.plan(pid, pw, E, tm)  # allocates the outputs once
+
+            def plan_call():
+                abi.moe_plan(pid, pw, Tp, K, E, tm, o["cnt"], o["eoff"], o["tiles"], o["stok"],
+                             o["sw"], o["pos"], o["boff"], o["meta"], o["scratch"])
+
+            us_p = timed_us(plan_call, max(args.steps, 20))
+            plan_sizes[str(Tp)] = {"us": round(us_p, 2),
+                                   "padded_rows": int(o["meta"][2].item()),
+                                   "nblk": int(o["meta"][1].item())}
+
+    # the same steps with row-major weights (moe_forward, the contract's call)
+    rowmajor = None
+    if packed is not None:
+        def step_rm():
+            for cx_, cids, cw in chunks:
+                abi.forward(cx_, cids, cw, wts["gate"], wts["up"], wts["down"], tm=tm,
+                            workspace=ws, out=out)
+
+        for _ in range(args.warmup):
+            step_rm()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            step_rm()
+        torch.cuda.synchronize()
+        ms_rm = (time.perf_counter() - t2) * 1e3 / args.steps
+        rowmajor = {"value": cfg.T * K / (ms_rm * 1e-3), "unit": "rows/s",
+                    "ms_per_step": ms_rm,
+                    "note": "moe_forward with the row-major weights, same inputs and steps"}
     us = {k: 1e3 * v[0] / max(v[1], 1) for k, v in st_all.items()}
     gu_us = 1e3 * st["gateup"][0] / max(st["gateup"][1], 1)  # from the timed steps
     gu_bytes = gateup_bytes(cfg, meta, T)
@@ -499,6 +598,14 @@ def main():
                         "is written before each step",
         "stages_gbs": {k: round(b / (us[k] * 1e3), 1) for k, b in stage_bytes(cfg, meta, T).items()
                        if us.get(k)},
+        "gather_us": round(gather_us, 2),
+        "plan_gather_combine": plan_gather_combine(
+            cfg, meta, T, us["hist"] + us["scan"] + us["place"], gather_us, us["combine"]),
+        "plan_us_by_T": plan_sizes or None,
+        "plan_us_by_T_note": "moe_plan alone (one launch up to 32,768 entries), 512 experts, "
+                             "top-10, tm 16, at the token counts of the page's plan table; "
+                             "padded_rows is the plan's nr",
+        "rowmajor": rowmajor,
         "step_us": step_us,
         "plan_meta": {n: int(v) for n, v in zip(abi.META_FIELDS, meta)},
         "stages_tflops": {k: round(v / (us[k] * 1e6), 1) for k, v in flops.items() if us.get(k)},
