@@ -81,6 +81,14 @@ def lib():
         L.oracle_route_topk.argtypes = [P, i64, i32, i32, P, P]
         L.oracle_combine_f32.restype = None
         L.oracle_combine_f32.argtypes = [P, P, i64, i32, i32, P]
+        L.oracle_y16_exponent.restype = i32
+        L.oracle_y16_exponent.argtypes = [ctypes.c_float]
+        for n in ("oracle_y16_encode", "oracle_y16_decode"):
+            getattr(L, n).restype = None
+        L.oracle_y16_encode.argtypes = [P, i64, i32, P, P]
+        L.oracle_y16_decode.argtypes = [P, P, i64, i32, P]
+        L.oracle_combine_y16.restype = None
+        L.oracle_combine_y16.argtypes = [P, P, P, i64, i32, i32, P]
         _lib = L
     return _lib
 
@@ -243,6 +251,47 @@ def combine_f32(Y: np.ndarray, pos: np.ndarray, T: int, K: int) -> np.ndarray:
     d = Y.shape[1]
     out = np.empty((T, d), np.float32)
     lib().oracle_combine_f32(_p(Y), _p(pos), T, K, d, _p(out))
+    return out
+
+
+# --------------------------------------------------- compact expert outputs --
+
+Y16_BLOCK = 128  # columns per exponent
+
+
+def y16_exponent(M: float) -> int:
+    """The exponent e of a block whose largest magnitude is M (see oracle.c)."""
+    return int(lib().oracle_y16_exponent(float(M)))
+
+
+def y16_encode(y: np.ndarray):
+    """fp32 rows [n, d] -> (binary16 bit patterns uint16 [n, d], exponents int8 [n, nb])."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    n, d = y.shape
+    s = np.empty((n, d), np.uint16)
+    e = np.empty((n, (d + Y16_BLOCK - 1) // Y16_BLOCK), np.int8)
+    lib().oracle_y16_encode(_p(y), n, d, _p(s), _p(e))
+    return s, e
+
+
+def y16_decode(s: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """Exact fp32 values s * 2^-e of compact rows."""
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    e = np.ascontiguousarray(e, dtype=np.int8)
+    n, d = s.shape
+    y = np.empty((n, d), np.float32)
+    lib().oracle_y16_decode(_p(s), _p(e), n, d, _p(y))
+    return y
+
+
+def combine_y16(s: np.ndarray, e: np.ndarray, pos: np.ndarray, T: int, K: int) -> np.ndarray:
+    """out[t] = fp32 sum over k ascending from +0.0f of the decoded compact rows pos[t*K+k]."""
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    e = np.ascontiguousarray(e, dtype=np.int8)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    d = s.shape[1]
+    out = np.empty((T, d), np.float32)
+    lib().oracle_combine_y16(_p(s), _p(e), _p(pos), T, K, d, _p(out))
     return out
 
 

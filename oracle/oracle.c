@@ -469,6 +469,73 @@ void oracle_combine_f32(const float *Y, const int32_t *pos, int64_t T, int K, in
 }
 
 /* ------------------------------------------------------------------------- */
+/* Compact expert outputs (a storage format of the layer's intermediate y,    */
+/* not a step of the pages): each row is cut into blocks of 128 columns (the  */
+/* last one may be shorter); a block holds binary16 values s[c] and one       */
+/* exponent e and stands for the values s[c] * 2^-e, exactly.                 */
+/* Encoding of fp32 values v[c]: M = the largest |v[c]| of the block (NaN     */
+/* ignored). If M is 0 or not finite, e = 0. Otherwise M = m * 2^k with m in  */
+/* [1/2, 1) and e = 15 - k, clamped to [-112, 100], so that M * 2^e lies in   */
+/* [2^14, 2^15). s[c] = v[c] * 2^e rounded to binary16, nearest even. The     */
+/* scaling by 2^e is exact, and over that range of e every decoded binary16   */
+/* value is an exact fp32 number.                                             */
+/* ------------------------------------------------------------------------- */
+#define Y16_BLOCK 128
+
+int oracle_y16_exponent(float M)
+{
+    if (!(M > 0.0f) || isinf(M))
+        return 0;
+    int k;
+    frexp((double)M, &k);
+    int e = 15 - k;
+    return e < -112 ? -112 : (e > 100 ? 100 : e);
+}
+
+void oracle_y16_encode(const float *y, int64_t nrows, int d, uint16_t *s, int8_t *ex)
+{
+    int nb = (d + Y16_BLOCK - 1) / Y16_BLOCK;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int b = 0; b < nb; ++b) {
+            int c0 = b * Y16_BLOCK, c1 = c0 + Y16_BLOCK < d ? c0 + Y16_BLOCK : d;
+            float M = 0.0f;
+            for (int c = c0; c < c1; ++c) M = fmaxf(M, fabsf(y[(size_t)r * d + c]));
+            int e = oracle_y16_exponent(M);
+            ex[(size_t)r * nb + b] = (int8_t)e;
+            for (int c = c0; c < c1; ++c)
+                s[(size_t)r * d + c] = oracle_f64_to_f16(ldexp((double)y[(size_t)r * d + c], e));
+        }
+}
+
+void oracle_y16_decode(const uint16_t *s, const int8_t *ex, int64_t nrows, int d, float *y)
+{
+    int nb = (d + Y16_BLOCK - 1) / Y16_BLOCK;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int c = 0; c < d; ++c)
+            y[(size_t)r * d + c] = (float)ldexp(oracle_f16_to_f64(s[(size_t)r * d + c]),
+                                                -(int)ex[(size_t)r * nb + c / Y16_BLOCK]);
+}
+
+/* The combine over compact rows: each value decoded exactly, then the same   */
+/* fp32 sum from +0.0f in k order as oracle_combine_f32.                      */
+void oracle_combine_y16(const uint16_t *s, const int8_t *ex, const int32_t *pos, int64_t T, int K,
+                        int d, float *out)
+{
+    int nb = (d + Y16_BLOCK - 1) / Y16_BLOCK;
+    for (int64_t t = 0; t < T; ++t)
+        for (int c = 0; c < d; ++c) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                int32_t r = pos[t * K + k];
+                if (r >= 0)
+                    acc = acc + (float)ldexp(oracle_f16_to_f64(s[(size_t)r * d + c]),
+                                             -(int)ex[(size_t)r * nb + c / Y16_BLOCK]);
+            }
+            out[t * d + c] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Router: [P1] s.1 finding 5 and s.3 name the kernel that writes the routed  */
 /* ids (route_topk); the workload description fixes what it computes: a      */
 /* softmax over the E router logits, the K largest probabilities kept and     */

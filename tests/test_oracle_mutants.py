@@ -33,6 +33,12 @@ MUTANTS = [
      ["test_oracle_formats.py"]),
     ("bf16_subnormal_flush", "double q = nearbyint(ldexp(a, 133));", "double q = 0.0 * a;",
      ["test_oracle_formats.py"]),
+    ("y16_exponent_off_by_one", "int e = 15 - k;", "int e = 16 - k;", ["test_oracle_y16.py"]),
+    ("y16_decode_wrong_sign", "y[(size_t)r * d + c] = (float)ldexp(oracle_f16_to_f64(s[(size_t)r * d + c]),\n                                                -(int)ex[",
+     "y[(size_t)r * d + c] = (float)ldexp(oracle_f16_to_f64(s[(size_t)r * d + c]),\n                                                +(int)ex[",
+     ["test_oracle_y16.py"]),
+    ("combine_y16_block_index", "-(int)ex[(size_t)r * nb + c / Y16_BLOCK]);\n            }",
+     "-(int)ex[(size_t)r * nb + c % nb]);\n            }", ["test_oracle_y16.py"]),
 ]
 
 
