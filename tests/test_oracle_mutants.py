@@ -26,8 +26,9 @@ MUTANTS = [
     ("skip_counted_as_bad", "if (e == -1)\n            nskip++;", "if (e == -2)\n            nskip++;",
      ["test_oracle_plan.py"]),
     ("gather_pad_not_zero", "memset(dst, 0, rb);", "(void)dst;", ["test_oracle_gather_combine.py"]),
-    ("combine_reversed", "for (int k = 0; k < K; ++k) {\n                int32_t r = pos[t * K + k];",
-     "for (int k = K - 1; k >= 0; --k) {\n                int32_t r = pos[t * K + k];",
+    ("combine_reversed",
+     "for (int k = 0; k < K; ++k) {\n                int32_t r = pos[t * K + k];\n                if (r >= 0)\n                    acc = acc + Y[",
+     "for (int k = K - 1; k >= 0; --k) {\n                int32_t r = pos[t * K + k];\n                if (r >= 0)\n                    acc = acc + Y[",
      ["test_oracle_gather_combine.py"]),
     ("f16_truncates", "double q = nearbyint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));",
      ["test_oracle_formats.py"]),
