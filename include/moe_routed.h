@@ -304,6 +304,19 @@ int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, 
  * the plan is one kernel that also writes the FFN's work list, and when x is
  * smaller than 2 GiB the gate/up kernel reads its rows from x through stok
  * (the gather is fused; the workspace's xs rows are then left unwritten).
+ * For fp16 and bf16 layers the expert outputs y are kept in a compact format,
+ * half the bytes of fp32 rows: each row is cut into blocks of 128 columns, a
+ * block holds binary16 values s and one exponent e (int8) and stands for
+ * s * 2^-e exactly; e puts the block's largest magnitude in [2^14, 2^15) (e =
+ * 15 - k for a maximum m * 2^k, m in [1/2, 1), clamped to [-112, 100]; 0 for
+ * an all-zero or infinite block) and s = y * 2^e rounded to binary16 (nearest
+ * even), a relative error of at most 2^-12 per value near the block maximum.
+ * The combine decodes each value exactly and sums in the same fixed order, so
+ * the result is deterministic; it differs in rounding from the four calls
+ * (whose y is fp32) but not from the same call again. In the workspace
+ * (moe_forward_layout) the y region then holds the binary16 rows [max_rows][d]
+ * followed by their exponents, block-major: [ceil(d/128)][max_rows]. fp32
+ * layers keep fp32 y and equal the four calls bit for bit.
  * In:  x [T][d] (dtype), ids [T*K], w [T*K], expert weights as above.
  * Out: out [T][d] fp32.
  * Errors: the union of the four calls' errors.

@@ -174,11 +174,13 @@ int gather_impl(const void *x, int dtype, int T, int d, const int32_t *stok, con
 
 // x != nullptr (moe_forward only): the gate/up kernel reads its rows from
 // x[stok[r]] (T rows) and xs is not used.
+// yexp != nullptr (moe_forward with 16-bit types): y receives the compact
+// format (binary16 rows, then yexp's block exponents) instead of fp32 rows.
 int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int dtype, int E,
              int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
              const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
              size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr, bool have_items = false,
-             const void *x = nullptr, int T = 0, bool packed = false)
+             const void *x = nullptr, int T = 0, bool packed = false, int8_t *yexp = nullptr)
 {
     const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                              y, scratch, scratch_bytes);
@@ -200,22 +202,26 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
     }
     {
         Rec r(tmr, s, MOE_STAGE_DOWN);
-        if (moe::launch_down(z, dtype, packed, h, wd, d, f, stok, sw, meta, scratch, y, s) !=
+        if (moe::launch_down(z, dtype, packed, h, wd, d, f, stok, sw, meta, scratch, y, yexp, s) !=
             hipSuccess)
             return MOE_EHIP;
     }
     return MOE_OK;
 }
 
+// yexp != nullptr: y holds the compact format (see ffn_impl)
 int combine_impl(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,
-                 float *out, hipStream_t s, moe_timer_t *tmr)
+                 float *out, hipStream_t s, moe_timer_t *tmr, const int8_t *yexp = nullptr)
 {
     if (T < 1 || K < 1 || d < 8 || d % 8 || max_rows < 1 || (int64_t)T * K > kI32Max)
         return MOE_EINVAL;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(pos, 4)) return MOE_EINVAL;
     Rec r(tmr, s, MOE_STAGE_COMBINE);
-    if (moe::launch_combine(y, max_rows, pos, T, K, d, out, s) != hipSuccess) return MOE_EHIP;
-    return MOE_OK;
+    const hipError_t e =
+        yexp ? moe::launch_combine_y16(reinterpret_cast<const uint16_t *>(y), yexp, max_rows, pos,
+                                       T, K, d, out, s)
+             : moe::launch_combine(y, max_rows, pos, T, K, d, out, s);
+    return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forward_layout_t *L,
@@ -276,12 +282,18 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
         rc = gather_impl(x, dtype, T, d, i32(L.stok), i32(L.meta), z.max_rows, b + L.xs, s, tmr);
         if (rc != MOE_OK) return rc;
     }
+    // 16-bit types: the expert outputs in the compact format, binary16 rows at
+    // L.y and their block exponents right after them (2d + ceil(d/128) bytes per
+    // row fit in the region's 4d)
+    int8_t *yexp = dtype == MOE_F32
+                       ? nullptr
+                       : reinterpret_cast<int8_t *>(b + L.y + (size_t)z.max_rows * d * 2);
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
                   fz.scratch_bytes, s, tmr, items,
-                  fused_gather ? x : nullptr, T, packed);
+                  fused_gather ? x : nullptr, T, packed, yexp);
     if (rc != MOE_OK) return rc;
-    return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr);
+    return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr, yexp);
 }
 
 }  // namespace

@@ -109,6 +109,51 @@ __device__ __forceinline__ int wave_max(int v)
     return __builtin_amdgcn_readlane(v, kWave - 1);
 }
 
+// maximum over the 16 lanes of each DPP row (lanes 16q .. 16q+15): xor-1 and
+// xor-2 quad permutes, then the mirrors within 8 and within 16 lanes. Every
+// lane of a row must be active (rows may differ).
+enum : int { kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140 };
+__device__ __forceinline__ int row16_max(int v)
+{
+    v = max(v, dpp_move<kQuadXor1>(v, v));
+    v = max(v, dpp_move<kQuadXor2>(v, v));
+    v = max(v, dpp_move<kRowHalfMirror>(v, v));
+    v = max(v, dpp_move<kRowMirror>(v, v));
+    return v;
+}
+
+// Compact expert outputs (moe_forward with 16-bit element types): each row of
+// y is cut into blocks of kY16Block columns; a block holds binary16 values s
+// and one exponent e (int8) and stands for s * 2^-e exactly. The exponents are
+// stored block-major, [block][max_rows], so that a wavefront's 64 rows of one
+// block are one contiguous 64-byte store. With M the
+// block's largest magnitude (NaN counted as 0), e = 15 - k for M = m * 2^k,
+// m in [1/2, 1), clamped to [-112, 100] (0 when M is 0 or infinite), so that
+// M * 2^e lies in [2^14, 2^15); s = v * 2^e rounded to binary16, nearest even.
+constexpr int kY16Block = 128;
+
+__device__ __forceinline__ int y16_exponent(float M)
+{
+    if (!(M > 0.0f) || __builtin_isinf(M)) return 0;
+    const int e = 15 - __builtin_amdgcn_frexp_expf(M);
+    return min(max(e, -112), 100);
+}
+
+// maximum over the 16 lanes of each DPP row of non-negative floats (fmax
+// ignores NaN, as the block maximum does); every lane of a row must be active
+__device__ __forceinline__ float row16_fmax(float v)
+{
+    v = __builtin_fmaxf(v, __int_as_float(dpp_move<kQuadXor1>(__float_as_int(v), 0)));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_move<kQuadXor2>(__float_as_int(v), 0)));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_move<kRowHalfMirror>(__float_as_int(v), 0)));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_move<kRowMirror>(__float_as_int(v), 0)));
+    return v;
+}
+
+// 2^e as a float, for e in [-126, 127]: scaling by it is exact (as ldexp)
+// wherever the product is a normal number
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }
+
 // Per-expert output ranges: lane l owns expert `expert` (its value in lane l)
 // with n entries. Each lane writes the first kOwnEntries entries of its own
 // expert; the rest of a heavy expert's entries are written by the whole

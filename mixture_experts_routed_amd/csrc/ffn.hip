@@ -424,7 +424,74 @@ struct GemmArgs {
     int nsplit;       // K splits per (item, column group)
     int split_steps;  // K-steps per split
     int skip_quads;   // 1: the items in runs of 4 (the first ctl[1]) are left to k_big
+    // down projection, compact outputs: out holds binary16 rows and yexp their
+    // exponents, block-major: yexp[b * estride + row] for the kY16Block columns
+    // of block b (estride = max_rows); nullptr: fp32 y
+    int8_t *yexp;
+    int64_t estride;
 };
+
+__device__ __forceinline__ void store_b64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v,
+                                          int policy_sc1)
+{
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    if (policy_sc1)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, v), r, off, 0, kSC1);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, v), r, off, 0, kNT);
+}
+
+// One row of a down cell in the compact format. This lane holds the row's
+// values v[m][c] at columns col + m * 64 + c; the 16 lanes of its DPP row hold
+// the row's columns [col0, col0 + 128), one exponent block. Lanes whose
+// columns lie past N contribute nothing and store nothing, but take part in
+// the row maximum (every lane of the row must be active here). ry covers the
+// item's rows of binary16 y; rl is the row within the item. Stores: sc1
+// (policy_sc1) or non-temporal. Returns the row's exponent (the same in all
+// 16 lanes); the caller stores the exponents (store_y16_exponents).
+__device__ __forceinline__ int store_y16_row(const GemmArgs &p, __amdgpu_buffer_rsrc_t ry, int rl,
+                                             int col, const float (&v)[2][4], int policy_sc1)
+{
+    constexpr int HALF = 16 * kNpl;
+    const int N = p.N;
+    float M = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            M = __builtin_fmaxf(M, col + m * HALF < N ? __builtin_fabsf(v[m][c]) : 0.0f);
+    const int e = y16_exponent(row16_fmax(M));
+    const float scale = pow2f(e);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        if (col + m * HALF >= N) continue;
+        float q[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = v[m][c] * scale;
+        store_b64(ry, (uint32_t)((rl * N + col + m * HALF) * 2),
+                  make_uint2(Elt<_Float16>::pack2(q[0], q[1]), Elt<_Float16>::pack2(q[2], q[3])),
+                  policy_sc1);
+    }
+    return e;
+}
+
+// The exponents of a wavefront's 64 rows of one block, in one store: ev[mt][r]
+// is the exponent of row 16 mt + 4 kg + r (kg = the lane's DPP row), so lane
+// (kg, nq) already holds row 16 (nq >> 2) + 4 kg + (nq & 3) -- the 64 lanes
+// hold the 64 rows once each -- and stores it if `real` (its row holds an
+// entry). yexp_block = the block's exponents, row0 = the item's first row.
+template <int NMT>
+__device__ __forceinline__ void store_y16_exponents(int8_t *yexp_block, int64_t row0,
+                                                    const int (&ev)[NMT][4], int rl, bool real)
+{
+    const int nq = threadIdx.x & 15;
+    int e = 0;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e = (mt == (nq >> 2) && r == (nq & 3)) ? ev[mt][r] : e;
+    if (real) yexp_block[row0 + rl] = (int8_t)e;
+}
 
 // Epilogue of one wavefront: acc[m][mt][c][r] is the output at row
 // 16*mt + 4*kg + r of item `it` and column col + c (+ HALF for m = 1 of the
@@ -437,8 +504,41 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
     constexpr int ES = sizeof(T);
     constexpr int HALF = GATEUP ? 0 : 16 * kNpl;
     const int N = p.N;
-    if (col >= N) return;
     const bool partial = MAY_SPLIT && p.nsplit > 1;
+    if constexpr (!GATEUP && ES == 2) {
+        if (p.yexp && !partial) {
+            // compact y: every lane stays for the row maxima (no early exit by column)
+            const int col0 = col - kNpl * (threadIdx.x & 15);
+            if (col0 >= N) return;  // the whole slice lies past N (wave-uniform)
+            const __amdgpu_buffer_rsrc_t ry =
+                make_rsrc(static_cast<uint16_t *>(p.out) + (int64_t)it.row0 * N,
+                          (uint32_t)(it.nrows * N * 2));
+            int ev[NMT][4];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ev[mt][r] = 0;
+                    const int rl = 16 * mt + 4 * kg + r;
+                    if (rl >= it.nrows) continue;  // uniform over the DPP row
+                    const float2 ri = rinfo[rl];
+                    if (__float_as_int(ri.y) < 0) continue;  // pad rows are never combined
+                    float v[2][4];
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) v[m][c] = ri.x * acc[m][mt][c][r];
+                    ev[mt][r] = store_y16_row(p, ry, rl, col, v, 1);
+                }
+            const int nq = threadIdx.x & 15;
+            const int rl = 16 * (nq >> 2) + 4 * kg + (nq & 3);
+            const bool real = rl < it.nrows && __float_as_int(rinfo[rl].y) >= 0;
+            store_y16_exponents<NMT>(p.yexp + (col0 / kY16Block) * p.estride, it.row0, ev, rl,
+                                     real);
+            return;
+        }
+    }
+    if (col >= N) return;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -1176,6 +1276,35 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
         // workgroups share in L2 (measured: down 1.83 -> 1.67 ms on the
         // one-call long prompt)
         constexpr int HALF = 16 * kNpl;
+        if (p.yexp) {
+            // compact y (binary16 + block exponents), the same rows and stores
+            const int col0 = BCOLS * cb + (BCOLS / 2) * wc;
+            if (col0 >= N) return;  // wave-uniform
+            const __amdgpu_buffer_rsrc_t ry16 =
+                make_rsrc(static_cast<uint16_t *>(p.out) + (int64_t)it.row0 * N,
+                          (uint32_t)(it.nrows * N * 2));
+            int ev[kMT][4];
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ev[mt][r] = 0;
+                    const int src = 16 * kg + 4 * mt + r;
+                    const float g = __shfl(rsw, src);
+                    if (__shfl(rtok, src) < 0) continue;  // uniform over the DPP row
+                    const int rl = 16 * mt + 4 * kg + r;
+                    float v[2][4];
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) v[m][c] = g * acc[m][mt][c][r];
+                    ev[mt][r] = store_y16_row(p, ry16, rl, col, v, 0);
+                }
+            // this lane holds the token of row 16 (nq >> 2) + 4 kg + (nq & 3)
+            store_y16_exponents<kMT>(p.yexp + (col0 / kY16Block) * p.estride, it.row0, ev,
+                                     16 * (nq >> 2) + 4 * kg + (nq & 3), rtok >= 0);
+            return;
+        }
         const __amdgpu_buffer_rsrc_t ry =
             make_rsrc(static_cast<float *>(p.out) + (int64_t)it.row0 * N, (uint32_t)(it.nrows * N * 4));
 #pragma unroll
@@ -1269,6 +1398,51 @@ __global__ __launch_bounds__(256) void k_reduce_down(const float *__restrict__ p
              make_float4(g * a.x, g * a.y, g * a.z, g * a.w));
 }
 
+// y in the compact format from the split planes: half a wavefront per (row,
+// exponent block), lane l of it taking columns kY16Block * b + 4 l .. + 3; a
+// unit's 32 lanes are all active or all not (the row decides), so the block
+// maximum runs over all of them
+template <int NS>
+__global__ __launch_bounds__(256) void k_reduce_down_y16(
+    const float *__restrict__ part, int64_t plane, int N, const int32_t *__restrict__ stok,
+    const float *__restrict__ sw, const int32_t *__restrict__ meta, int64_t max_rows,
+    uint16_t *__restrict__ y, int8_t *__restrict__ yexp, int nyb)
+{
+    // (exponents block-major: yexp[b * max_rows + row])
+    const int64_t unit = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+    const int l = threadIdx.x & 31;
+    const int64_t row = unit / nyb;
+    const int b = (int)(unit - row * nyb);
+    if (row >= rows_of_plan(meta, max_rows) || stok[row] < 0) return;
+    const int c = b * kY16Block + 4 * l;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < N) {
+        const float *P = part + row * N + c;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float4 v = *reinterpret_cast<const float4 *>(P + s * plane);
+            a = make_float4(a.x + v.x, a.y + v.y, a.z + v.z, a.w + v.w);
+        }
+    }
+    const float g = sw[row];
+    const float v[4] = {g * a.x, g * a.y, g * a.z, g * a.w};
+    float M = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) M = __builtin_fmaxf(M, c < N ? __builtin_fabsf(v[q]) : 0.0f);
+    M = row16_fmax(M);
+    M = __builtin_fmaxf(M, __shfl_xor(M, 16));  // the unit's other 16 lanes
+    const int e = y16_exponent(M);
+    if (c < N) {
+        const float scale = pow2f(e);
+        float q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = v[k] * scale;
+        store_nt(reinterpret_cast<uint2 *>(y + row * N + c),
+                 make_uint2(Elt<_Float16>::pack2(q[0], q[1]), Elt<_Float16>::pack2(q[2], q[3])));
+    }
+    if (l == 0) yexp[b * max_rows + row] = (int8_t)e;
+}
+
 // ---- host launchers --------------------------------------------------------
 // the reductions' launch for a split count in [2, kMaxSplit] (any other count
 // is refused)
@@ -1298,6 +1472,22 @@ hipError_t reduce_down(int nsplit, dim3 grid, hipStream_t s, const float *part, 
                                        y);
         hipLaunchKernelGGL((k_reduce_down<NS>), grid, dim3(256), 0, s, part, plane, N, stok, sw,
                            meta, max_rows, y);
+        return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int NS = 2>
+hipError_t reduce_down_y16(int nsplit, dim3 grid, hipStream_t s, const float *part, int64_t plane,
+                           int N, const int32_t *stok, const float *sw, const int32_t *meta,
+                           int64_t max_rows, uint16_t *y, int8_t *yexp, int nyb)
+{
+    if constexpr (NS <= kMaxSplit) {
+        if (nsplit != NS)
+            return reduce_down_y16<NS + 1>(nsplit, grid, s, part, plane, N, stok, sw, meta,
+                                           max_rows, y, yexp, nyb);
+        hipLaunchKernelGGL((k_reduce_down_y16<NS>), grid, dim3(256), 0, s, part, plane, N, stok,
+                           sw, meta, max_rows, y, yexp, nyb);
         return hipSuccess;
     }
     return hipErrorInvalidValue;
@@ -1379,7 +1569,7 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
 template <typename T, bool PACKED>
 hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f,
                   const int32_t *stok, const float *sw, const int32_t *meta, const void *scratch,
-                  float *y, hipStream_t s)
+                  void *y, int8_t *yexp, hipStream_t s)
 {
     GemmArgs p = gemm_args(z, scratch, false);
     p.A = h;
@@ -1389,6 +1579,12 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
     p.out = y;
     p.Kd = f;
     p.N = d;
+    int nyb = 0;
+    if constexpr (sizeof(T) == 2) {
+        p.yexp = yexp;
+        p.estride = z.max_rows;
+        nyb = (d + kY16Block - 1) / kY16Block;
+    }
     if constexpr (PACKED && sizeof(T) == 2) {
         if (z.big_dn && z.blocks_big_dn > 0) {
             p.skip_quads = 1;
@@ -1399,8 +1595,13 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
     hipLaunchKernelGGL((k_expert_gemm<T, false, false, PACKED>), dim3((unsigned)z.blocks_dn),
                        dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch));
     if (z.split_dn > 1) {
-        const hipError_t e = reduce_down(p.nsplit, dim3(reduce_blocks(z.max_rows, d)), s, p.part,
-                                         p.plane, d, stok, sw, meta, z.max_rows, y);
+        const hipError_t e =
+            p.yexp ? reduce_down_y16(p.nsplit,
+                                     dim3((unsigned)((z.max_rows * nyb * 32 + 255) / 256)), s,
+                                     p.part, p.plane, d, stok, sw, meta, z.max_rows,
+                                     static_cast<uint16_t *>(y), p.yexp, nyb)
+                   : reduce_down(p.nsplit, dim3(reduce_blocks(z.max_rows, d)), s, p.part,
+                                 p.plane, d, stok, sw, meta, z.max_rows, static_cast<float *>(y));
         if (e != hipSuccess) return e;
     }
     return hipGetLastError();
@@ -1442,16 +1643,16 @@ hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, con
 
 hipError_t launch_down(const FfnShape &z, int dtype, bool packed, const void *h, const void *wd,
                        int d, int f, const int32_t *stok, const float *sw, const int32_t *meta,
-                       const void *scratch, float *y, hipStream_t s)
+                       const void *scratch, void *y, int8_t *yexp, hipStream_t s)
 {
     if (dtype == 1)
-        return packed ? down_t<_Float16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
-                      : down_t<_Float16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+        return packed ? down_t<_Float16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, yexp, s)
+                      : down_t<_Float16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, yexp, s);
     if (dtype == 2)
-        return packed ? down_t<__bf16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
-                      : down_t<__bf16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
-    return packed ? down_t<float, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, s)
-                  : down_t<float, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, s);
+        return packed ? down_t<__bf16, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, yexp, s)
+                      : down_t<__bf16, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, yexp, s);
+    return packed ? down_t<float, true>(z, h, wd, d, f, stok, sw, meta, scratch, y, nullptr, s)
+                  : down_t<float, false>(z, h, wd, d, f, stok, sw, meta, scratch, y, nullptr, s);
 }
 
 }  // namespace moe

@@ -12,8 +12,6 @@
 
 namespace moe {
 
-constexpr int kRowsPerBlock = 4;  // one wave per row, 4 waves per workgroup
-
 // non-temporal accesses for data touched once here (the destination rows of
 // the gather, the expert outputs read by the combine, the layer output)
 __device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
@@ -35,49 +33,95 @@ __device__ __forceinline__ float4 load_nt(const float4 *p)
 
 // xs[r] = x[stok[r]] (bit copy) for r < min(meta[NR], max_rows); zeros on pad
 // rows. vpr = 16-byte vectors per row.
-__global__ __launch_bounds__(256) void k_gather(const uint4 *__restrict__ x, int T, int vpr,
-                                                const int32_t *__restrict__ stok,
-                                                const int32_t *__restrict__ meta, int64_t max_rows,
-                                                uint4 *__restrict__ xs)
+// A token's row is copied to up to K rows, in no particular order of r. To
+// fetch each token row into one L2 only, row r is copied by the XCD
+// (stok[r] mod 8) of its token (a pad row by r mod 8): workgroup b scans the
+// kGatherWaves x 64 rows of row group b / 8 and copies those owned by
+// XCD b mod 8 (the hardware deals the workgroups of a 1-D grid to the 8 XCDs
+// round robin). Each row has exactly one owner whatever the placement; only
+// the L2 reuse depends on it. A wavefront copies its matching rows
+// kGatherBatch at a time, with kGatherVec loads per lane and row in flight.
+constexpr int kGatherWaves = 4;
+constexpr int kGatherBatch = 4;
+constexpr int kGatherVec = 4;
+
+__global__ __launch_bounds__(kGatherWaves * kWave) void k_gather(
+    const uint4 *__restrict__ x, int T, int vpr, const int32_t *__restrict__ stok,
+    const int32_t *__restrict__ meta, int64_t max_rows, uint4 *__restrict__ xs)
 {
-    const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int xcd = blockIdx.x & 7;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t r0 = ((int64_t)(blockIdx.x >> 3) * kGatherWaves + wave) * kWave;
     const int64_t nr = min((int64_t)meta[kMetaNr], max_rows);
-    if (r >= nr) return;
+    if (r0 >= nr) return;
     const int lane = threadIdx.x & 63;
-    const int t = stok[r];
-    uint4 *dst = xs + r * vpr;
-    if ((unsigned)t < (unsigned)T) {
-        const uint4 *src = x + (int64_t)t * vpr;
-        int j = lane;
-        for (; j + 3 * kWave < vpr; j += 4 * kWave) {  // 4 loads in flight per lane
-            const uint4 a = src[j], b = src[j + kWave], c = src[j + 2 * kWave],
-                        d = src[j + 3 * kWave];
-            store_nt(dst + j, a);
-            store_nt(dst + j + kWave, b);
-            store_nt(dst + j + 2 * kWave, c);
-            store_nt(dst + j + 3 * kWave, d);
+    const int64_t r = r0 + lane;
+    const int t = r < nr ? stok[r] : -1;
+    const int owner = (unsigned)t < (unsigned)T ? (t & 7) : (int)(r & 7);
+    uint64_t mine = __ballot(r < nr && owner == xcd);
+    while (mine) {
+        int64_t rr[kGatherBatch];  // -1: empty slot of the batch
+        int tt[kGatherBatch];
+#pragma unroll
+        for (int u = 0; u < kGatherBatch; ++u) {
+            rr[u] = -1;
+            tt[u] = -1;
+            if (mine) {
+                const int src = __ffsll((unsigned long long)mine) - 1;
+                mine &= mine - 1;
+                rr[u] = r0 + src;
+                tt[u] = __builtin_amdgcn_readlane(t, src);
+            }
         }
-        for (; j < vpr; j += kWave) store_nt(dst + j, src[j]);
-    } else {
-        for (int j = lane; j < vpr; j += kWave) store_nt(dst + j, make_uint4(0u, 0u, 0u, 0u));
+        for (int j0 = lane; j0 < vpr; j0 += kGatherVec * kWave) {
+            uint4 v[kGatherBatch][kGatherVec];
+#pragma unroll
+            for (int u = 0; u < kGatherBatch; ++u)
+#pragma unroll
+                for (int q = 0; q < kGatherVec; ++q) {
+                    const int j = j0 + q * kWave;
+                    v[u][q] = (j < vpr && (unsigned)tt[u] < (unsigned)T)
+                                  ? x[(int64_t)tt[u] * vpr + j]
+                                  : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+            for (int u = 0; u < kGatherBatch; ++u)
+#pragma unroll
+                for (int q = 0; q < kGatherVec; ++q) {
+                    const int j = j0 + q * kWave;
+                    if (j < vpr && rr[u] >= 0) store_nt(xs + rr[u] * vpr + j, v[u][q]);
+                }
+        }
     }
 }
 
 // out[t] = (((+0 + y[pos[tK]]) + y[pos[tK+1]]) + ...) in fp32, k ascending,
 // pos < 0 or >= max_rows skipped. One workgroup per token, sized to cover a
-// whole row (one float4 column per lane up to 1024 lanes); for a column, the
-// rows of up to kCombineGroup entries are loaded first (independent loads, all
-// in flight), then added in k order, so one memory latency covers a group.
+// whole row (up to 1024 lanes); a lane takes 4 columns of fp32 rows, or 8
+// columns of compact rows (Y16: binary16 values, and the exponent e of their
+// 128-column block, block-major: yexp[b * max_rows + row]; each value decoded
+// exactly as s * 2^-e). For a lane's
+// columns, the rows of up to kCombineGroup entries are loaded first -- every
+// load issued, a skipped entry reading row 0 and adding nothing -- then added
+// in k order, so one memory latency covers a group.
 constexpr int kCombineGroup = 16;
 
-__global__ __launch_bounds__(1024) void k_combine(const float4 *__restrict__ y, int64_t max_rows,
-                                                 int vpr, const int32_t *__restrict__ pos, int T,
-                                                 int K, float4 *__restrict__ out)
+template <bool Y16>
+__global__ __launch_bounds__(1024) void k_combine(const void *__restrict__ y,
+                                                 const int8_t *__restrict__ yexp,
+                                                 int64_t max_rows, int d,
+                                                 const int32_t *__restrict__ pos, int T, int K,
+                                                 float4 *__restrict__ out)
 {
+    constexpr int COLS = Y16 ? 8 : 4;  // columns per lane
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const int t = blockIdx.x;
     const int32_t *p = pos + (int64_t)t * K;
-    for (int j = threadIdx.x; j < vpr; j += blockDim.x) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int nvec = d / COLS;
+    for (int j = threadIdx.x; j < nvec; j += blockDim.x) {
+        float acc[COLS];
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) acc[c] = 0.f;
         for (int k0 = 0; k0 < K; k0 += kCombineGroup) {
             const int n = min(kCombineGroup, K - k0);
             int row[kCombineGroup];
@@ -86,21 +130,38 @@ __global__ __launch_bounds__(1024) void k_combine(const float4 *__restrict__ y, 
                 const int r = u < n ? p[k0 + u] : -1;  // wave-uniform: scalar loads
                 row[u] = (r >= 0 && r < max_rows) ? r : -1;
             }
-            float4 v[kCombineGroup];
+            u4 raw[kCombineGroup];
+            int e[kCombineGroup];
 #pragma unroll
-            for (int u = 0; u < kCombineGroup; ++u)
-                v[u] = row[u] >= 0 ? load_nt(y + (int64_t)row[u] * vpr + j)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int u = 0; u < kCombineGroup; ++u) {
+                const int64_t r = row[u] >= 0 ? row[u] : 0;
+                raw[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u4 *>(y) + r * nvec + j);
+                e[u] = Y16 ? -(int)yexp[(int64_t)((j * COLS) / kY16Block) * max_rows + r] : 0;
+            }
 #pragma unroll
-            for (int u = 0; u < kCombineGroup; ++u)
-                if (row[u] >= 0) {
-                    acc.x += v[u].x;
-                    acc.y += v[u].y;
-                    acc.z += v[u].z;
-                    acc.w += v[u].w;
+            for (int u = 0; u < kCombineGroup; ++u) {
+                if (row[u] < 0) continue;  // wave-uniform
+                // the loaded words as plain values (a bit cast takes values, not
+                // vector elements)
+                const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                if constexpr (Y16) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const uint16_t hbits = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
+                        acc[c] += __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, hbits),
+                                                          e[u]);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[c] += __builtin_bit_cast(float, w[c]);
                 }
+            }
         }
-        store_nt(out + (int64_t)t * vpr + j, acc);
+#pragma unroll
+        for (int c = 0; c < COLS; c += 4)
+            store_nt(out + (int64_t)t * (d / 4) + j * (COLS / 4) + c / 4,
+                     make_float4(acc[c], acc[c + 1], acc[c + 2], acc[c + 3]));
     }
 }
 
@@ -108,8 +169,9 @@ hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int3
                          const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s)
 {
     const int vpr = d * elem_bytes / 16;
-    const int64_t blocks = (max_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(k_gather, dim3((unsigned)blocks), dim3(256), 0, s,
+    constexpr int rows_per_group = kGatherWaves * kWave;
+    const int64_t blocks = (max_rows + rows_per_group - 1) / rows_per_group * 8;
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)blocks), dim3(kGatherWaves * kWave), 0, s,
                        static_cast<const uint4 *>(x), T, vpr, stok, meta, max_rows,
                        static_cast<uint4 *>(xs));
     return hipGetLastError();
@@ -118,11 +180,18 @@ hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int3
 hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K,
                           int d, float *out, hipStream_t s)
 {
-    const int vpr = d / 4;
-    const int threads = min(1024, (vpr + kWave - 1) / kWave * kWave);
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(threads), 0, s,
-                       reinterpret_cast<const float4 *>(y), max_rows, vpr, pos, T, K,
-                       reinterpret_cast<float4 *>(out));
+    const int threads = min(1024, (d / 4 + kWave - 1) / kWave * kWave);
+    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(threads), 0, s, y, nullptr, max_rows, d, pos,
+                       T, K, reinterpret_cast<float4 *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_y16(const uint16_t *y16, const int8_t *yexp, int64_t max_rows,
+                              const int32_t *pos, int T, int K, int d, float *out, hipStream_t s)
+{
+    const int threads = min(1024, (d / 8 + kWave - 1) / kWave * kWave);
+    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(threads), 0, s, y16, yexp, max_rows, d, pos,
+                       T, K, reinterpret_cast<float4 *>(out));
     return hipGetLastError();
 }
 

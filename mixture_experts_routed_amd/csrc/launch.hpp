@@ -35,6 +35,9 @@ hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int3
                          const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s);
 hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K,
                           int d, float *out, hipStream_t s);
+// the combine over compact expert outputs (binary16 rows y16, block exponents yexp)
+hipError_t launch_combine_y16(const uint16_t *y16, const int8_t *yexp, int64_t max_rows,
+                              const int32_t *pos, int T, int K, int d, float *out, hipStream_t s);
 
 // ---- grouped expert FFN ----
 // rows per work item of the grouped GEMMs
@@ -72,9 +75,12 @@ hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *
 hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
                                   const int32_t *meta, const void *scratch, void *h, hipStream_t s);
+// yexp == nullptr: y is fp32 [rows][d]; otherwise (16-bit types only) y holds
+// binary16 rows and yexp [rows][ceil(d / 128)] their block exponents (the
+// compact format of common.hpp)
 hipError_t launch_down(const FfnShape &z, int dtype, bool packed, const void *h, const void *wd,
                        int d, int f, const int32_t *stok, const float *sw, const int32_t *meta,
-                       const void *scratch, float *y, hipStream_t s);
+                       const void *scratch, void *y, int8_t *yexp, hipStream_t s);
 
 // ---- packed expert weights ----
 // bytes of one packed matrix set: gate/up matrices [E][d][f] (gateup = true,

@@ -229,22 +229,48 @@ def test_forward_skipped_entries():
     assert np.all(got[5] == 0) and not np.any(np.signbit(got[5]))
 
 
-@pytest.mark.parametrize("cfg", [synth.CONFIGS["decode_bf16"], synth.CONFIGS["tiny_fp32"],
-                                 PATHS[0], custom("no_split_f16", T=2048, d=2048, E=64, K=4,
-                                                  f=1024, dtype="f16")],
-                         ids=["decode_bf16_split_both", "tiny_fp32_split_down",
-                              "split_both_bf16", "no_split_f16"])
-def test_forward_equals_the_four_calls(cfg):
-    """moe_forward (one-launch plan, gather fused into gate/up, and, when the
-    down projection is split along K, the combine adding the split partials
-    itself) returns the same bits as moe_plan, moe_gather, moe_expert_ffn and
-    moe_combine called one by one"""
+def compact_outputs(ws, cfg, T, K):
+    """moe_forward's expert outputs in the compact format, read from its workspace:
+    binary16 rows [R, d] (uint16 bits), their block exponents as [R, nb] (int8;
+    stored block-major, [nb][R]), the entry rows pos and the plan's nr"""
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    L = abi.moe_forward_layout(T, K, cfg.E, cfg.d, cfg.f, cfg.tm, dt)
+    R = abi.moe_plan_sizes(T, K, cfg.E, cfg.tm).max_rows
+    nb = (cfg.d + 127) // 128
+    raw = ws.cpu().numpy()
+    s16 = raw[L.y: L.y + R * cfg.d * 2].view(np.uint16).reshape(R, cfg.d)
+    ex = raw[L.y + R * cfg.d * 2: L.y + R * cfg.d * 2 + R * nb].view(np.int8).reshape(nb, R).T
+    ex = np.ascontiguousarray(ex)
+    pos = raw[L.pos: L.pos + 4 * T * K].view(np.int32)
+    stok = raw[L.stok: L.stok + 4 * R].view(np.int32)
+    nr = int(raw[L.meta: L.meta + 44].view(np.int32)[2])
+    return s16, ex, pos, stok, nr
+
+
+FOUR = [synth.CONFIGS["decode_bf16"], synth.CONFIGS["tiny_fp32"], PATHS[0],
+        custom("no_split_f16", T=2048, d=2048, E=64, K=4, f=1024, dtype="f16"),
+        custom("ragged_d_bf16", T=300, d=328, E=12, K=3, f=200, dtype="bf16", x_std=1.0)]
+
+
+@pytest.mark.parametrize("cfg", FOUR, ids=["decode_bf16_split_gateup", "tiny_fp32_split_down",
+                                           "split_both_bf16", "no_split_f16", "ragged_d_bf16"])
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_forward_equals_the_four_calls(cfg, packed):
+    """moe_forward (one-launch plan, gather fused into gate/up) against moe_plan,
+    moe_gather, moe_expert_ffn and moe_combine called one by one. fp32 layers: the
+    same bits. fp16/bf16 layers keep the expert outputs in the compact format: its
+    rows equal the oracle's encoding of the four calls' fp32 rows bit for bit, and
+    its output equals the oracle's fixed-order combine over them bit for bit"""
     case = make_case(cfg)
-    say(f"[forward vs four calls] {cfg.name}")
+    say(f"[forward vs four calls] {cfg.name} packed={packed}")
     T, K = case.ids.shape
     dt = abi.DTYPE_NAME[cfg.dtype]
     x, ids, w = dev(case.x, cfg.dtype), dev(case.ids), dev(case.w)
-    a, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm)
+    pk = abi.pack(case.d("wg"), case.d("wu"), case.d("wd")) if packed else None
+    wts = (pk["gate"], pk["up"], pk["down"]) if packed else (case.d("wg"), case.d("wu"),
+                                                              case.d("wd"))
+    a, ws = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                        packed=pk)
     p = abi.plan(ids, w, cfg.E, cfg.tm)
     R = p["sizes"].max_rows
     xs = torch.empty((R, cfg.d), dtype=x.dtype, device="cuda")
@@ -253,12 +279,42 @@ def test_forward_equals_the_four_calls(cfg):
     y = torch.empty((R, cfg.d), dtype=torch.float32, device="cuda")
     scratch = torch.empty(abi.moe_ffn_scratch_bytes(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt),
                           dtype=torch.uint8, device="cuda")
-    abi.moe_expert_ffn(xs, case.d("wg"), case.d("wu"), case.d("wd"), dt, cfg.E, cfg.d, cfg.f,
-                       cfg.tm, p["eoff"], p["stok"], p["sw"], p["meta"], R, h, y, scratch)
+    ffn = abi.moe_expert_ffn_packed if packed else abi.moe_expert_ffn
+    ffn(xs, *wts, dt, cfg.E, cfg.d, cfg.f, cfg.tm, p["eoff"], p["stok"], p["sw"], p["meta"], R,
+        h, y, scratch)
     b = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
     abi.moe_combine(y, R, p["pos"], T, K, cfg.d, b)
     torch.cuda.synchronize()
-    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    if cfg.dtype == "f32":
+        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+    else:
+        s16, ex, pos, stok, nr = compact_outputs(ws, cfg, T, K)
+        real = np.nonzero(stok[:nr] >= 0)[0]
+        want_s, want_e = oracle.y16_encode(host(y)[real])
+        assert np.array_equal(s16[real], want_s)
+        assert np.array_equal(ex[real], want_e)
+        out = oracle.combine_y16(s16, ex, pos, T, K)
+        assert np.array_equal(host(a).view(np.uint32), out.view(np.uint32))
+    case.drop_device()
+
+
+@pytest.mark.parametrize("name", ["prefill_fp16", "ubatch_bf16", "prefill_tailskip_fp16"])
+def test_forward_combine_over_compact_outputs_full_size(name):
+    """at full size (packed weights, as the benchmark runs it), every token's output
+    is the oracle's fixed-order combine over the layer's own compact expert
+    outputs, bit for bit"""
+    cfg = synth.CONFIGS[name]
+    case = make_case(cfg)
+    say(f"[forward compact combine] {name}")
+    pk = abi.pack(case.d("wg"), case.d("wu"), case.d("wd"))
+    out, ws = abi.forward(dev(case.x, cfg.dtype), dev(case.ids), dev(case.w), case.d("wg"),
+                          case.d("wu"), case.d("wd"), tm=cfg.tm, packed=pk)
+    torch.cuda.synchronize()
+    T, K = case.ids.shape
+    s16, ex, pos, _, _ = compact_outputs(ws, cfg, T, K)
+    want = oracle.combine_y16(s16, ex, pos, T, K)
+    assert np.array_equal(host(out).view(np.uint32), want.view(np.uint32))
+    del pk, ws
     case.drop_device()
 
 

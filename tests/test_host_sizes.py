@@ -8,7 +8,9 @@ oracle's plan of their routing,
     (split x max_rows x 2f for gate/up, split x max_rows x d for down; the two
     projections share the region), the work list rounded up to 256 bytes;
   * moe_forward_layout carves every intermediate, at its full bound, from the
-    workspace moe_forward_workspace asks for, without overlaps."""
+    workspace moe_forward_workspace asks for, without overlaps; for 16-bit
+    layers the compact expert outputs (binary16 rows and their block
+    exponents) fit in the y region."""
 import numpy as np
 import pytest
 
@@ -49,6 +51,10 @@ def test_sizes_cover_the_layer(cfg):
             "sw": R * 4, "pos": nent * 4, "boff": z.nblk * E * 4, "meta": 11 * 4,
             "plan_scratch": z.scratch_bytes, "xs": R * cfg.d * es, "h": R * cfg.f * es,
             "y": R * cfg.d * 4, "ffn_scratch": scratch}
+    if cfg.dtype != "f32":
+        # 16-bit layers keep y compact: binary16 rows, then one exponent byte per
+        # 128 columns, inside the fp32-sized region
+        assert R * cfg.d * 2 + R * ((cfg.d + 127) // 128) <= need["y"]
     spans = sorted((getattr(L, k), getattr(L, k) + n, k) for k, n in need.items())
     for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
         assert a1 <= b0, (ka, kb)

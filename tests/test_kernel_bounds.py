@@ -263,3 +263,39 @@ def test_model_catches_an_undersized_grid():
                                                      len(items) + 9, axis=0)])
     with pytest.raises(AssertionError):
         model_projection(cfg, None, R, cfg.T, True, True, True, 1, 80, False, short, 0)
+
+
+GATHER_CASES = [synth.CONFIGS[n] for n in ("prefill_fp16", "decode_bf16", "tiny_fp32",
+                                           "prefill_tailskip_fp16")] + SHAPES[:24]
+
+
+@pytest.mark.parametrize("cfg", GATHER_CASES, ids=[c.name for c in GATHER_CASES])
+def test_gather_partition_copies_every_row_once_in_bounds(cfg):
+    """the standalone gather's grid (row groups of 4 x 64 rows, 8 workgroups per
+    group, one per XCD) and its ownership rule (token mod 8, a pad row by row mod 8)
+    copy every row below nr exactly once, read only token rows below T and write
+    only rows below nr"""
+    T = cfg.tokens_per_call
+    ids, w = synth.routing(cfg, T)
+    R = abi.moe_plan_sizes(T, cfg.K, cfg.E, cfg.tm).max_rows
+    p = oracle.plan(ids, w, cfg.E, cfg.tm)
+    nr = len(p["stok"])
+    stok = np.full(R, -1, np.int64)
+    stok[:nr] = p["stok"]
+    blocks = ceil(R, 256) * 8
+    copies = np.zeros(nr, np.int64)
+    for b in range(blocks):
+        for wave in range(4):
+            r0 = ((b >> 3) * 4 + wave) * 64
+            if r0 >= nr:
+                continue
+            r = np.arange(r0, r0 + 64)
+            ok = r < nr
+            t = np.where(ok, stok[np.minimum(r, R - 1)], -1)
+            owner = np.where((t >= 0) & (t < T), t & 7, r & 7)
+            mine = r[ok & (owner == (b & 7))]
+            assert np.all(mine < nr)
+            tt = stok[mine]
+            assert np.all((tt < T))  # tokens read are rows of x (pads read nothing)
+            copies[mine] += 1
+    assert np.all(copies == 1)
