@@ -107,15 +107,35 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def gemm_is_gateup(name: str) -> bool:
-    """k_expert_gemm<T, GATEUP, GATHERED, PACKED>: GATEUP from the (mangled or
-    demangled) kernel name"""
+def gemm_flags(name: str):
+    """k_expert_gemm<T, GATEUP, GATHERED, PACKED>: the three flags from the (mangled
+    or demangled) kernel name, or None"""
     import re
-    m = re.search(r"k_expert_gemmI(?:DF16_|DF16b|f)Lb([01])E", name)
+    m = re.search(r"k_expert_gemmI(?:DF16_|DF16b|f)Lb([01])ELb([01])ELb([01])E", name)
     if m:
-        return m.group(1) == "1"
-    m = re.search(r"k_expert_gemm<[^,]+,\s*(true|false)", name)
-    return bool(m) and m.group(1) == "true"
+        return tuple(g == "1" for g in m.groups())
+    m = re.search(r"k_expert_gemm<[^,]+,\s*(true|false),\s*(true|false),\s*(true|false)", name)
+    return tuple(g == "true" for g in m.groups()) if m else None
+
+
+def gemm_is_gateup(name: str) -> bool:
+    """GATEUP of a k_expert_gemm kernel name"""
+    f = gemm_flags(name)
+    return bool(f) and f[0]
+
+
+def kernel_short_name(name: str) -> str:
+    """a kernel's name in the traffic record: k_expert_gemm/gateup or /down (packed
+    weights; _rowmajor with row-major ones), else the kernel's own name with its
+    template arguments"""
+    import re
+    if "k_expert_gemm" in name:
+        f = gemm_flags(name) or (False, False, True)
+        return f"k_expert_gemm/{'gateup' if f[0] else 'down'}{'' if f[2] else '_rowmajor'}"
+    m = re.search(r"moe::(k_\w+(?:<[^>]*>)?)|_ZN3moe(\d+)(k_\w+?)I", name)
+    if m:
+        return m.group(1) or m.group(3)
+    return name[:40]
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> dict:
@@ -124,7 +144,6 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> 
     (the --copy-calibration-mib copy in the same run). Writes a markdown summary with a
     machine-readable record line and returns the record."""
     import csv
-    import re
     from collections import defaultdict
 
     def per_kernel(path, counter):
@@ -136,13 +155,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, command: str) -> 
             d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
         return vals
 
-    def short(name):
-        m = re.search(r"moe::(k_\w+)|_ZN3moe(\d+)(k_\w+?)I", name)
-        if "k_expert_gemm" in name:
-            return f"k_expert_gemm/{'gateup' if gemm_is_gateup(name) else 'down'}"
-        if m:
-            return m.group(1) or m.group(3)
-        return name[:40]
+    short = kernel_short_name
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     copy_kib = None
@@ -265,17 +278,25 @@ def stage_flops(cfg, meta):
     return {"gateup": 2 * nreal * cfg.d * 2 * cfg.f, "down": 2 * nreal * cfg.f * cfg.d}
 
 
+def y_row_bytes(cfg):
+    """bytes of one expert-output row as moe_forward keeps it: fp32 for fp32 layers;
+    for fp16/bf16 the compact format (binary16 values and one exponent byte per
+    128 columns)"""
+    return cfg.d * 4 if cfg.dtype == "f32" else cfg.d * 2 + (cfg.d + 127) // 128
+
+
 def stage_bytes(cfg, meta, T):
     """Algorithmic HBM bytes of each HBM-bound kernel of one moe_forward call."""
     es = 2 if cfg.dtype != "f32" else 4
     nactive, nr, nent = int(meta[4]), int(meta[2]), int(meta[0])
     nreal = nent - int(meta[6]) - int(meta[7])  # rows that hold an entry
+    yb = y_row_bytes(cfg)
     return {
         "gateup": gateup_bytes(cfg, meta, T),
         # down: W_down of the active experts, h read, y written on real rows
-        "down": nactive * cfg.f * cfg.d * es + nr * cfg.f * es + nreal * cfg.d * 4,
+        "down": nactive * cfg.f * cfg.d * es + nr * cfg.f * es + nreal * yb,
         # combine: y rows of every entry read, out written, pos read
-        "combine": nreal * cfg.d * 4 + T * cfg.d * 4 + nent * 4,
+        "combine": nreal * yb + T * cfg.d * 4 + nent * 4,
     }
 
 
@@ -568,7 +589,10 @@ def main():
     else:
         roof = {"kernel": "gateup_swiglu", "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": recorded_traffic("k_expert_gemm/gateup"),
+                # the committed counter record covers the prefill workload only
+                "traffic": recorded_traffic("k_expert_gemm/gateup" +
+                                            ("" if packed is not None else "_rowmajor"))
+                           if cfg.name == "prefill_fp16" else None,
                 "algorithmic_bytes_per_launch": gu_bytes}
     rows = cfg.T * K
     res = {

@@ -131,3 +131,14 @@ def test_read_probe_is_outside_the_layer_library_and_rejects_bad_arguments():
     assert L.bench_stream_read(None, 1 << 20, A, 16, None) == 1
     assert L.bench_stream_read(A, 1 << 20, A + 2, 16, None) == 1  # sink not 4-byte aligned
     del ctypes
+
+
+def test_kernel_short_names_keep_the_weight_layout_and_variant_apart():
+    rowmajor = GATEUP.replace("Lb1ELb1ELb1E", "Lb1ELb1ELb0E")
+    assert bench.kernel_short_name(GATEUP) == "k_expert_gemm/gateup"
+    assert bench.kernel_short_name(rowmajor) == "k_expert_gemm/gateup_rowmajor"
+    assert bench.kernel_short_name(DOWN) == "k_expert_gemm/down"
+    assert bench.kernel_short_name("void moe::k_combine<true>(void const*, signed char const*, "
+                                   "long, int, int const*, int, int, "
+                                   "HIP_vector_type<float, 4u>*)") == "k_combine<true>"
+    assert bench.kernel_short_name(COMBINE) == "k_combine"
