@@ -22,7 +22,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // The grouped FFN works on items of at most kItemRows rows of one expert; its
 // scratch holds ctl (first kCtlBytes: ctl[0] = items, ctl[1] = items in runs
-// of 4 when they come first in the list, else 0) followed by the items.
+// of 4 when they come first in the list, else 0, ctl[2] = items in runs of 2
+// or 4) followed by the items.
 constexpr int kItemRows = 64;
 constexpr size_t kCtlBytes = 256;
 

@@ -53,6 +53,8 @@ constexpr int kNpl = 4;                 // columns per lane and B stream
 // output columns per 8-wavefront big-cell workgroup: h columns (gate/up) or y
 // columns (down)
 constexpr int big_cols(bool gateup) { return gateup ? 128 : 256; }
+// output columns per narrow-cell workgroup (one slice of h, one of y)
+constexpr int narrow_cols(bool gateup) { return gateup ? 64 : 128; }
 
 int ffn_rows_per_item() { return kItemRows; }
 
@@ -170,6 +172,9 @@ int group_cols(bool gateup) { return kWavesPerBlock * (gateup ? 16 * kNpl : 32 *
 // projection's 123 cells, each streaming 2.9 MB, take 51 us split 5 ways
 // (3: 54, 4: 52; 6 ways no longer fits one round of workgroups: 61).
 constexpr int64_t kSplitBelowCells = 192;
+// packed 16-bit projections with fewer wide cells than this run on narrow
+// cells (a decode layer: 41 items x 3 (gate/up) or x 6 (down) column groups)
+constexpr int64_t kNarrowBelowCells = 512;
 constexpr int64_t kTargetCells = 512;
 // The 8-wavefront kernel takes the runs of 4 items when the plan bound allows
 // this many rows per expert on average.
@@ -206,9 +211,16 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
     split_for(z.max_items * gs_dn, f, kstep, &z.split_dn, &z.steps_dn);
     z.blocks_gu = (z.max_items * gs_gu * z.split_gu + 7) / 8 * 8;
     z.blocks_dn = (z.max_items * gs_dn * z.split_dn + 7) / 8 * 8;
+    // big cells (packed 16-bit weights, experts with hundreds of rows); narrow
+    // cells (packed 16-bit weights, few rows per expert) when the wide cells
+    // would leave the GPU short of workgroups
     const bool big = dtype != 0 && max_rows >= kBigMinRowsPerExpert * (int64_t)E;
     z.big_gu = big && z.split_gu == 1;
     z.big_dn = big && z.split_dn == 1;
+    z.narrow_gu = dtype != 0 && !big && z.max_items * gs_gu < kNarrowBelowCells;
+    z.narrow_dn = dtype != 0 && !big && z.max_items * gs_dn < kNarrowBelowCells;
+    z.blocks_narrow_gu = (z.max_items * ((f + narrow_cols(true) - 1) / narrow_cols(true)) + 7) / 8 * 8;
+    z.blocks_narrow_dn = (z.max_items * ((d + narrow_cols(false) - 1) / narrow_cols(false)) + 7) / 8 * 8;
     z.blocks_big_gu = (ffn_max_quads(max_rows) * ((f + big_cols(true) - 1) / big_cols(true)) + 7) / 8 * 8;
     z.blocks_big_dn = (ffn_max_quads(max_rows) * ((d + big_cols(false) - 1) / big_cols(false)) + 7) / 8 * 8;
     z.plane_gu = max_rows * 2 * (int64_t)f;
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
                                                    WorkItem *__restrict__ items, int max_items,
                                                    int runs_first)
 {
-    __shared__ int s_q[16], s_r[16];
+    __shared__ int s_q[16], s_r[16], s_p[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int r0 = 0, rows = 0;
     if (tid < E) {
@@ -242,24 +254,28 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ e
     const int n4 = n & ~3;
     const int qincl = wave_inclusive_scan(n4, lane);
     const int rincl = wave_inclusive_scan(n - n4, lane);
+    const int pairs = wave_sum(n - n4 >= 2 ? 2 : 0);  // items in this wave's runs of 2
     if (lane == 63) {
         s_q[wv] = qincl;
         s_r[wv] = rincl;
+        s_p[wv] = pairs;
     }
     __syncthreads();
-    int qbefore = qincl - n4, rbefore = rincl - (n - n4), qtotal = 0, rtotal = 0;
+    int qbefore = qincl - n4, rbefore = rincl - (n - n4), qtotal = 0, rtotal = 0, ptotal = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         qbefore += (q < wv) ? s_q[q] : 0;
         rbefore += (q < wv) ? s_r[q] : 0;
         qtotal += s_q[q];
         rtotal += s_r[q];
+        ptotal += s_p[q];
     }
     wave_fill_items(n, r0, rows, qbefore, rbefore, qtotal, runs_first != 0, tid, lane, max_items,
                     (int)max_rows, items);
     if (tid == 0) {
         ctl[0] = min(qtotal + rtotal, max_items);
         ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
+        ctl[2] = min(qtotal + ptotal, max_items);
     }
 }
 
@@ -278,6 +294,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // Cache policy of a buffer load: 0 = default; kNT = non-temporal (the weights
 // are read exactly once, so they should not displace the reused row tiles).
 constexpr int kNT = 2;
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maximum (no wait)
+constexpr int wait_vm(int n) { return 0x0F70 | n; }
 
 template <int BYTES, int POLICY = 0> struct Ld;
 template <int POLICY> struct Ld<8, POLICY> {
@@ -305,6 +324,11 @@ __device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
 {
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(u2{v.x, v.y}, reinterpret_cast<u2 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
+{
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u4{v.x, v.y, v.z, v.w}, reinterpret_cast<u4 *>(p));
 }
 
 // Stores of the down projection's y, which the combine reads next: buffer
@@ -630,10 +654,22 @@ constexpr int kLdsU4 = 2 * tall_buf_u4(2) > 2 * kATileU4 ? 2 * tall_buf_u4(2) : 
 //    MFMAs of step s; the loop body is straight-line code, so they stay in
 //    flight. The per-step barrier keeps the 4 wavefronts in step, so together
 //    they read 4 adjacent row segments of every weight row.
+//  * depth of the weight stream, one policy per launch (ctl[2]): when most
+//    items are single (each streams its expert's weights from HBM once) the
+//    launch runs shallow: the row operand's K-tail mask is applied as it is
+//    loaded, so a wavefront waits for the step it has just issued (all but
+//    its last few loads) before computing, about one step per wavefront in
+//    flight. More only queues in the memory system: on a 2,048-token prefill
+//    layer (512 experts, single items) masking at the use, with S-1 steps in
+//    flight, was 4% slower. When most items are in runs (skewed routing; the
+//    runs' tiles are re-read from L2) the mask moves to the use and the ring
+//    keeps S-1 steps in flight: 7% faster on the down projection of a skewed
+//    2,048-token chunk. Shallow single items beside deep runs in one launch
+//    measured slower than either policy.
 // GATHERED (gate/up only): A is the token activation x [a_rows][Kd] and row r
 // of the item reads x[stok[r]] -- the gather fused into the A-tile loads.
 // The K range is [kb, ke) (a split of the reduction, or all of it).
-template <typename T, bool GATEUP, bool GATHERED, bool PACKED, int NMT>
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool DEEP, int NMT>
 __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it, int slice,
                                            int kb, int ke, int split, uint4 *__restrict__ a_lds,
                                            float2 *__restrict__ rinfo)
@@ -742,13 +778,16 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
         for (int i = 0; i < NB; ++i) st.b[1][i] = Ld<LBB, kNT>::run(rb1, vb, (uint32_t)i * rowb);
         // K past the range: the weights read as zero; zero A too so that no
         // non-finite value of a neighbouring row can leak in as 0 * inf.
+        // Shallow: masked here, which makes the wavefront wait for the step's
+        // loads right after issuing them; deep: masked at its use
         const int ka = k0 + achunk;
-        const uint32_t am = ka < ke ? 0xffffffffu : 0u;
-        st.a = mask4(Ld<16>::run(ra, va0 + (uint32_t)ka * ES, 0u), am);
+        st.a = Ld<16>::run(ra, va0 + (uint32_t)ka * ES, 0u);
+        if constexpr (!DEEP) st.a = mask4(st.a, ka < ke ? 0xffffffffu : 0u);
     };
     auto compute = [&](const Stage &st, int step) {
         uint4 *slot = a_lds + (step & 1) * kATileU4;
-        slot[tid] = st.a;
+        const int ka = kb + step * KSTEP + achunk;
+        slot[tid] = DEEP ? mask4(st.a, ka < ke ? 0xffffffffu : 0u) : st.a;
         __syncthreads();
         uint4 af[NMT];
 #pragma unroll
@@ -788,8 +827,13 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
     constexpr int S = stages_for(NMT);
     const int nsteps = (ke - kb + KSTEP - 1) / KSTEP;
     Stage st[S];
+    // deep: the prologue's loads stay in step order (the load-count waits at
+    // the loop head are taken over both entries into it)
 #pragma unroll
-    for (int j = 0; j < S - 1; ++j) load(st[j], kb + j * KSTEP);
+    for (int j = 0; j < S - 1; ++j) {
+        load(st[j], kb + j * KSTEP);
+        if constexpr (DEEP) __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s = 0; s < nsteps; s += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
@@ -817,7 +861,7 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
 // Every wavefront computes 4 m-tiles (a short last item computes zero rows).
 // The weight loads keep the default cache policy here: the other runs of the
 // same expert read the same tile, often while it is still in L2.
-template <typename T, bool GATEUP, bool GATHERED, bool PACKED, int R>
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool DEEP, int R>
 __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__restrict__ items,
                                            int i0, int nitems, int g, int j, int kb, int ke,
                                            int split, uint4 *__restrict__ lds,
@@ -934,16 +978,24 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
         const uint32_t vb = vpb + (uint32_t)((k0 - kb) / KSTEP) * bstep;
 #pragma unroll
         for (int i = 0; i < PNB; ++i) st.b[i] = Ld<LBB>::run(rbp, vb, (uint32_t)i * rowb);
+        // A past the K range masked here (shallow) or at its use (deep), as in
+        // the wide cells
         const int ka = k0 + KR * kg;
         const uint32_t am = ka < ke ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-            st.a[mt] = mask4(Ld<16>::run(ra, va[mt] + (uint32_t)ka * ES, 0u), am);
+        for (int mt = 0; mt < NMT; ++mt) {
+            st.a[mt] = Ld<16>::run(ra, va[mt] + (uint32_t)ka * ES, 0u);
+            if constexpr (!DEEP) st.a[mt] = mask4(st.a[mt], am);
+        }
     };
     // fragment (or fp32 row) q of lane l of slice s, matrix m in a buffer
     auto frag = [&](int s, int m, int q, int l) { return ((s * NMAT + m) * 4 + q) * 64 + l; };
     auto compute = [&](const Stage &st, int step) {
         uint4 *buf = lds + (step & 1) * BUF;
+        const uint32_t am = kb + step * KSTEP + KR * kg < ke ? 0xffffffffu : 0u;
+        uint4 a[NMT];
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) a[mt] = DEEP ? mask4(st.a[mt], am) : st.a[mt];
         if constexpr (PACKED) {
 #pragma unroll
             for (int i = 0; i < PNB; ++i) buf[frag(pcs, pm, PNB * hh + i, plu)] = st.b[i];
@@ -971,7 +1023,7 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
                     const uint4 fb = buf[frag(cs, m, c, lane)];
 #pragma unroll
                     for (int mt = 0; mt < NMT; ++mt)
-                        acc[m][mt][c] = Elt<T>::mfma(st.a[mt], fb, acc[m][mt][c]);
+                        acc[m][mt][c] = Elt<T>::mfma(a[mt], fb, acc[m][mt][c]);
                 }
         } else {
 #pragma unroll
@@ -984,7 +1036,7 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
 #pragma unroll
                         for (int mt = 0; mt < NMT; ++mt)
                             acc[m][mt][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                lanef(st.a[mt], q), lanef(bq, c), acc[m][mt][c], 0, 0, 0);
+                                lanef(a[mt], q), lanef(bq, c), acc[m][mt][c], 0, 0, 0);
                 }
         }
     };
@@ -995,7 +1047,10 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
     const int nsteps = (ke - kb + KSTEP - 1) / KSTEP;
     Stage st[S];
 #pragma unroll
-    for (int jj = 0; jj < S - 1; ++jj) load(st[jj], kb + jj * KSTEP);
+    for (int jj = 0; jj < S - 1; ++jj) {  // as in the wide cells
+        load(st[jj], kb + jj * KSTEP);
+        if constexpr (DEEP) __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s = 0; s < nsteps; s += S) {
 #pragma unroll
         for (int jj = 0; jj < S; ++jj) {
@@ -1006,6 +1061,35 @@ __device__ __forceinline__ void tall_cells(const GemmArgs &p, const WorkItem *__
         }
     }
     store_cells<T, GATEUP, NMT>(p, it, col, kg, acc, my_rinfo, split);
+}
+
+// The cell of item i: a tall cell for an item in a run, else a wide cell.
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool DEEP>
+__device__ __forceinline__ void gemm_cell(const GemmArgs &p, const WorkItem *__restrict__ items,
+                                          const WorkItem it, int i, int nitems, int g, int kb,
+                                          int ke, int split, uint4 *__restrict__ lds,
+                                          float2 *__restrict__ rinfo)
+{
+    const int run = it.run & 0xff, j = (it.run >> 8) & 0xff;
+    if (run == 4 && j < 4 && i >= j) {
+        tall_cells<T, GATEUP, GATHERED, PACKED, DEEP, 4>(p, items, i - j, nitems, g, j, kb, ke,
+                                                         split, lds, rinfo);
+        return;
+    }
+    if (run == 2 && j < 2 && i >= j) {
+        tall_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, items, i - j, nitems, g, j, kb, ke,
+                                                         split, lds, rinfo);
+        return;
+    }
+    // wave-uniform by construction, so the buffer descriptors live in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = g * kWavesPerBlock + wave;
+    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
+    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    default: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    }
 }
 
 // One workgroup per (work item, group of 4 column slices, K split).
@@ -1031,26 +1115,14 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     const int kb = split * p.split_steps * KSTEP;
     const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
     const WorkItem it = items[i];
-    const int run = it.run & 0xff, j = (it.run >> 8) & 0xff;
-    if (run == 4 && j < 4 && i >= j) {
-        tall_cells<T, GATEUP, GATHERED, PACKED, 4>(p, items, i - j, nitems, g, j, kb, ke, split,
-                                                   lds, rinfo);
-        return;
-    }
-    if (run == 2 && j < 2 && i >= j) {
-        tall_cells<T, GATEUP, GATHERED, PACKED, 2>(p, items, i - j, nitems, g, j, kb, ke, split,
-                                                   lds, rinfo);
-        return;
-    }
-    // wave-uniform by construction, so the buffer descriptors live in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slice = g * kWavesPerBlock + wave;
-    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    default: wide_cells<T, GATEUP, GATHERED, PACKED, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    }
+    // weight-stream depth of the launch: deep when at least half the items are
+    // in runs, else shallow (the same for every workgroup)
+    if (2 * ctl[2] >= nitems)
+        gemm_cell<T, GATEUP, GATHERED, PACKED, true>(p, items, it, i, nitems, g, kb, ke, split, lds,
+                                                     rinfo);
+    else
+        gemm_cell<T, GATEUP, GATHERED, PACKED, false>(p, items, it, i, nitems, g, kb, ke, split,
+                                                      lds, rinfo);
 }
 
 // ---- big cells: runs of 4 items on 8 wavefronts (packed, 16-bit) ------------
@@ -1087,9 +1159,6 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
 constexpr int kBigThreads = 512;
 constexpr int kDeepAU4 = 4 * kItemRows * 4;   // A tile of one step: 256 rows x 4 chunks
 constexpr int kDeepBufU4 = kDeepAU4 + 1024;   // + B: 16 KB = 32 KB per buffer
-// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maximum (no wait)
-constexpr int wait_vm(int n) { return 0x0F70 | n; }
-
 template <typename T, bool GATEUP, bool GATHERED>
 __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
                                                       const int32_t *__restrict__ ctl,
@@ -1326,6 +1395,261 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     }
 }
 
+// ---- narrow cells: small batches (decode), packed 16-bit weights -----------
+// With few work items (a handful of tokens: about one row per expert), the
+// wide cells above leave the GPU short of workgroups, and splitting K costs a
+// reduction. A narrow cell instead gives each wavefront one 16-column MFMA
+// fragment of a packed tile (1 KB per K-step and matrix, contiguous) over the
+// whole K range, with a deep register pipeline: a decode layer's gate/up
+// projection becomes ~1,400 wavefronts each streaming its weights with
+// kNarrowStages steps in flight, and no reduction.
+//  * gate/up: a workgroup of 4 wavefronts = one work item x one 64-column
+//    slice of h; wavefront c computes fragment c (columns 4j + c of the slice)
+//    of W_gate and W_up;
+//  * down: a workgroup of 8 wavefronts = one work item x one 128-column slice
+//    of y (one exponent block of the compact format); wavefront (m, c)
+//    computes fragment c of stream m (columns 64 m + 4j + c);
+//  * A (the item's rows) is loaded by every wavefront for its own MFMAs, only
+//    for rows that hold an entry (pad rows and rows past the item read zeros
+//    without memory traffic);
+//  * each accumulator sees the same MFMA sequence as in an unsplit wide cell,
+//    so the results are the same bits;
+//  * epilogue through LDS: the fragments' outputs are written to a row-major
+//    LDS tile and stored as 16-byte row pieces; the compact y's row maxima are
+//    reduced over the 8 wavefronts of the block in LDS.
+constexpr int narrow_waves(bool gateup) { return gateup ? 4 : 8; }
+// register pipeline depth for NMT m-tiles: a stage holds the B fragments (8
+// VGPRs gate/up, 4 down) and NMT A fragments (4 VGPRs each)
+constexpr int narrow_stages(bool gateup, int nmt)
+{
+    return gateup ? (nmt == 1 ? 12 : nmt == 2 ? 8 : 6) : (nmt == 1 ? 16 : nmt == 2 ? 10 : 8);
+}
+
+template <typename T, bool GATEUP, bool GATHERED, int NMT>
+__device__ __forceinline__ void narrow_cell(const GemmArgs &p, const WorkItem it, int cb,
+                                            char *__restrict__ lds)
+{
+    constexpr int ES = 2;
+    constexpr int KSTEP = 32;
+    constexpr int NMAT = GATEUP ? 2 : 1;
+    constexpr int NW = narrow_waves(GATEUP);
+    constexpr int NC = narrow_cols(GATEUP);
+    constexpr int S = narrow_stages(GATEUP, NMT);
+    const int Kd = p.Kd, N = p.N;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nq = lane & 15, kg = lane >> 4;
+    const int c = wave & 3, m = wave >> 2;  // fragment, stream (down)
+
+    // B: this wavefront's fragment in each K-step's packed tile
+    const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
+    const int slice = cb;  // of 64 (gate/up) or 128 (down) columns
+    const int g = slice >> 2, w = slice & 3;
+    const bool slice_ok = slice * NC < N;  // workgroup-uniform
+    const size_t gbase = ((size_t)it.expert * z.gs + g) * z.nst * z.step_bytes;
+    const uint32_t grange = slice_ok ? (uint32_t)z.nst * z.step_bytes : 0u;
+    const uint32_t vb = (uint32_t)(w * z.m + (GATEUP ? 0 : m)) * 4096u + (uint32_t)c * 1024u +
+                        (uint32_t)lane * 16u;
+    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
+    const __amdgpu_buffer_rsrc_t rb1 =
+        make_rsrc(static_cast<const char *>(GATEUP ? p.B1 : p.B0) + gbase, grange);
+
+    // A: row 16 mt + nq of the item, K chunk kg; rows without an entry read
+    // zeros (offset past the descriptor's range)
+    __amdgpu_buffer_rsrc_t ra;
+    uint32_t va[NMT];
+    if constexpr (GATHERED) ra = make_rsrc(p.A, (uint32_t)((size_t)p.a_rows * Kd * ES));
+    else
+        ra = make_rsrc(static_cast<const T *>(p.A) + (size_t)it.row0 * Kd,
+                       (uint32_t)((size_t)it.nrows * Kd * ES));
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+        const int rl = 16 * mt + nq;
+        const int t = rl < it.nrows ? p.stok[it.row0 + rl] : -1;
+        if constexpr (GATHERED)
+            va[mt] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES
+                                                      : 0x80000000u;
+        else
+            va[mt] = t >= 0 ? (uint32_t)rl * (uint32_t)Kd * ES : 0x80000000u;
+    }
+
+    float4_t acc[NMAT][NMT];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) acc[q][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Stage {
+        uint4 b[NMAT];
+        uint4 a[NMT];
+    };
+    auto load = [&](Stage &st, int s) {
+        const uint32_t o = vb + (uint32_t)s * z.step_bytes;
+        st.b[0] = Ld<16, kNT>::run(rb0, o, 0u);
+        if constexpr (GATEUP) st.b[1] = Ld<16, kNT>::run(rb1, o, 0u);
+        const int ka = s * KSTEP + 8 * kg;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) st.a[mt] = Ld<16>::run(ra, va[mt] + (uint32_t)ka * ES, 0u);
+    };
+    auto compute = [&](const Stage &st, int s) {
+        // A masked past K at its use (a mask at the load would make the
+        // wavefront wait for the load)
+        const uint32_t am = s * KSTEP + 8 * kg < Kd ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+                acc[q][mt] = Elt<T>::mfma(mask4(st.a[mt], am), st.b[q], acc[q][mt]);
+    };
+    const int nsteps = z.nst;
+    Stage st[S];
+#pragma unroll
+    for (int j = 0; j < S - 1; ++j) {  // in step order, as in the wide cells
+        load(st[j], j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += S) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            // steps past the end load zeros (past the descriptors' ranges)
+            load(st[(j + S - 1) % S], s0 + j + S - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(st[j], s0 + j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // epilogue: lane (nq, kg) holds rows 16 mt + 4 kg + r of column 4 nq + c
+    // (+ 64 m for down) of the workgroup's NC columns
+    const int colw = 4 * nq + c + 64 * (GATEUP ? 0 : m);  // column within the tile
+    if constexpr (GATEUP) {
+        // h = D(silu(g) * u), every row of the item (pad rows give 0)
+        T *tile = reinterpret_cast<T *>(lds);  // [64 rows][64 columns]
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tile[(16 * mt + 4 * kg + r) * NC + colw] =
+                    (T)(silu(acc[0][mt][r]) * acc[1][mt][r]);
+        __syncthreads();
+        // 16-byte pieces: 8 per row
+        for (int q = tid; q < 16 * NMT * (NC / 8); q += NW * 64) {
+            const int row = q / (NC / 8), piece = q - row * (NC / 8);
+            const int col = slice * NC + 8 * piece;
+            if (row < it.nrows && col < N)
+                store_nt(reinterpret_cast<uint4 *>(static_cast<T *>(p.out) +
+                                                   ((int64_t)it.row0 + row) * N + col),
+                         *reinterpret_cast<const uint4 *>(tile + row * NC + 8 * piece));
+        }
+    } else {
+        // y = sw * acc on rows that hold an entry
+        float *rw = reinterpret_cast<float *>(lds);          // [64] router weights
+        int *rok = reinterpret_cast<int *>(rw + 64);         // [64] row holds an entry
+        float *mx = reinterpret_cast<float *>(rok + 64);     // [8 waves][64] row maxima
+        char *tile = reinterpret_cast<char *>(mx + NW * 64); // [64 rows][128 columns]
+        if (tid < 64) {
+            const bool real = tid < it.nrows && p.stok[it.row0 + tid] >= 0;
+            rw[tid] = real ? p.sw[it.row0 + tid] : 0.0f;
+            rok[tid] = real;
+        }
+        __syncthreads();
+        const bool compact = p.yexp != nullptr;
+        float v[NMT][4];
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[mt][r] = rw[16 * mt + 4 * kg + r] * acc[0][mt][r];
+            }
+        if (compact) {
+            // this wavefront's maximum of each row over its 16 columns (columns
+            // past N count 0), then over the 8 wavefronts
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = slice * NC + colw < N ? __builtin_fabsf(v[mt][r]) : 0.f;
+                    const float M = row16_fmax(a);
+                    if (nq == 0) mx[wave * 64 + 16 * mt + 4 * kg + r] = M;
+                }
+            __syncthreads();
+            int ev[NMT][4];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mt + 4 * kg + r;
+                    float M = 0.f;
+#pragma unroll
+                    for (int q = 0; q < NW; ++q) M = __builtin_fmaxf(M, mx[q * 64 + row]);
+                    ev[mt][r] = y16_exponent(M);
+                    reinterpret_cast<_Float16 *>(tile)[row * NC + colw] =
+                        (_Float16)(v[mt][r] * pow2f(ev[mt][r]));
+                }
+            // the block's exponents: one byte per row, by the lanes of wave 0
+            // (lane (kg, nq) holds row 16 (nq >> 2) + 4 kg + (nq & 3))
+            if (wave == 0) {
+                const int rl = 16 * (nq >> 2) + 4 * kg + (nq & 3);
+                store_y16_exponents<NMT>(p.yexp + (int64_t)slice * p.estride, it.row0, ev, rl,
+                                         rl < it.nrows && rok[rl]);
+            }
+            __syncthreads();
+            for (int q = tid; q < 16 * NMT * (NC / 8); q += NW * 64) {
+                const int row = q / (NC / 8), piece = q - row * (NC / 8);
+                const int col = slice * NC + 8 * piece;
+                if (row < it.nrows && rok[row] && col < N)
+                    store_nt(reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) +
+                                                       ((int64_t)it.row0 + row) * N + col),
+                             *reinterpret_cast<const uint4 *>(tile + (row * NC + 8 * piece) * 2));
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    reinterpret_cast<float *>(tile)[(16 * mt + 4 * kg + r) * NC + colw] = v[mt][r];
+            __syncthreads();
+            for (int q = tid; q < 16 * NMT * (NC / 4); q += NW * 64) {
+                const int row = q / (NC / 4), piece = q - row * (NC / 4);
+                const int col = slice * NC + 4 * piece;
+                if (row < it.nrows && rok[row] && col < N)
+                    store_nt(reinterpret_cast<float4 *>(static_cast<float *>(p.out) +
+                                                        ((int64_t)it.row0 + row) * N + col),
+                             *reinterpret_cast<const float4 *>(tile + (row * NC + 4 * piece) * 4));
+            }
+        }
+    }
+}
+
+// LDS of a narrow cell: gate/up a [64][64] tile of D; down the router weights,
+// the row maxima of 8 wavefronts and a [64][128] fp32 tile
+constexpr int narrow_lds_bytes(bool gateup)
+{
+    return gateup ? 64 * 64 * 2 : (64 + 64 + 8 * 64) * 4 + 64 * 128 * 4;
+}
+
+// One workgroup per (work item, column slice), XCD-contiguous.
+template <typename T, bool GATEUP, bool GATHERED>
+__global__ __launch_bounds__(narrow_waves(GATEUP) * 64) void k_narrow(
+    const GemmArgs p, const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items)
+{
+    static_assert(sizeof(T) == 2, "narrow cells: 16-bit element types");
+    __shared__ __attribute__((aligned(16))) char lds[narrow_lds_bytes(GATEUP)];
+    constexpr int NC = narrow_cols(GATEUP);
+    const int ncb = (p.N + NC - 1) / NC;
+    const int nitems = ctl[0];
+    const int lb = xcd_logical_block(nitems * ncb);
+    if (lb < 0) return;  // whole workgroup: no barrier reached
+    const int i = lb / ncb, cb = lb - i * ncb;
+    const WorkItem it = items[i];
+    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
+    case 1: narrow_cell<T, GATEUP, GATHERED, 1>(p, it, cb, lds); break;
+    case 2: narrow_cell<T, GATEUP, GATHERED, 2>(p, it, cb, lds); break;
+    case 3: narrow_cell<T, GATEUP, GATHERED, 3>(p, it, cb, lds); break;
+    default: narrow_cell<T, GATEUP, GATHERED, kMT>(p, it, cb, lds); break;
+    }
+}
+
 // ---- split-K reductions (fixed split order) --------------------------------
 __device__ __forceinline__ int rows_of_plan(const int32_t *meta, int64_t max_rows)
 {
@@ -1540,6 +1864,16 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     p.N = f;
     const dim3 grid((unsigned)z.blocks_gu);
     if constexpr (PACKED && sizeof(T) == 2) {
+        if (z.narrow_gu) {
+            const dim3 ngrid((unsigned)z.blocks_narrow_gu), nthreads(narrow_waves(true) * 64);
+            if (gathered)
+                hipLaunchKernelGGL((k_narrow<T, true, true>), ngrid, nthreads, 0, s, p,
+                                   ctl_of(scratch), items_of(scratch));
+            else
+                hipLaunchKernelGGL((k_narrow<T, true, false>), ngrid, nthreads, 0, s, p,
+                                   ctl_of(scratch), items_of(scratch));
+            return hipGetLastError();
+        }
         if (z.big_gu && z.blocks_big_gu > 0) {
             p.skip_quads = 1;
             const dim3 bgrid((unsigned)z.blocks_big_gu);
@@ -1586,6 +1920,12 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
         nyb = (d + kY16Block - 1) / kY16Block;
     }
     if constexpr (PACKED && sizeof(T) == 2) {
+        if (z.narrow_dn) {
+            hipLaunchKernelGGL((k_narrow<T, false, false>), dim3((unsigned)z.blocks_narrow_dn),
+                               dim3(narrow_waves(false) * 64), 0, s, p, ctl_of(scratch),
+                               items_of(scratch));
+            return hipGetLastError();
+        }
         if (z.big_dn && z.blocks_big_dn > 0) {
             p.skip_quads = 1;
             hipLaunchKernelGGL((k_big<T, false, false>), dim3((unsigned)z.blocks_big_dn),

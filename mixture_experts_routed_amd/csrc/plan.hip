@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
 {
     __shared__ int s_tot[kMaxExperts], s_before[kMaxExperts], s_eoff[kMaxExperts];
     __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
-    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16];
+    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16],
+        s_psum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x;
     const int bstart = b * kPlanBlock;
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int nit4 = nit & ~3;
     const int qincl = wave_inclusive_scan(nit4, lane);
     const int rincl = wave_inclusive_scan(nit - nit4, lane);
+    const int pairs = wave_sum(nit - nit4 >= 2 ? 2 : 0);  // items in this wave's runs of 2
     if (lane == 63) {
         s_sum[wv] = incl;
         s_qsum[wv] = qincl;
@@ -280,6 +282,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         s_max[wv] = mx;
         s_skip[wv] = skip;
         s_bad[wv] = bad;
+        s_psum[wv] = pairs;
     }
     __syncthreads();
     int before = 0, total = 0, qbefore = qincl - nit4, rbefore = rincl - (nit - nit4);
@@ -315,9 +318,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             wave_fill_items(mine ? nit : 0, start, rows, qbefore, rbefore, qtotal,
                             runs_first != 0, tid, lane, max_items, max_rows, items);
         if (b == 0 && tid == 0) {
-            int nact = 0, maxc = 0, nskip = 0, nbad = 0;
+            int nact = 0, maxc = 0, nskip = 0, nbad = 0, ptotal = 0;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
+                ptotal += s_psum[q];
                 nact += s_act[q];
                 maxc = max(maxc, s_max[q]);
                 nskip += s_skip[q];
@@ -338,6 +342,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             if (items) {
                 ctl[0] = min(qtotal + rtotal, max_items);
                 ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
+                ctl[2] = min(qtotal + ptotal, max_items);
             }
         }
     }

@@ -152,7 +152,7 @@ def worklist_model(eoff, E, max_rows, runs_first=True):
     all experts come first (ascending expert), then the others (ascending
     expert), or, without runs_first, each expert's items together by expert;
     run = length | index << 8. Returns (items [n, 4], items in runs of 4 when
-    they come first, else 0)."""
+    they come first, else 0, items in runs of 2 or 4)."""
     quad, rest = [], []
     for e in range(E):
         a = min(max(int(eoff[e]), 0), max_rows)
@@ -168,7 +168,8 @@ def worklist_model(eoff, E, max_rows, runs_first=True):
                 run = 1
             (quad if q < n4 or not runs_first else rest).append(
                 (e, a + 64 * q, min(64, b - a - 64 * q), run))
-    return np.array(quad + rest, np.int32).reshape(-1, 4), len(quad) if runs_first else 0
+    items = np.array(quad + rest, np.int32).reshape(-1, 4)
+    return items, len(quad) if runs_first else 0, int(np.sum((items[:, 3] & 0xFF) > 1))
 
 
 WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3, f=64,
@@ -181,8 +182,8 @@ WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3
 def test_worklist_layout(cfg, fused, packed):
     """the work list the FFN kernels consume (written by the worklist kernel
     for moe_expert_ffn, by the one-launch plan for moe_forward) equals the
-    model above; the runs of 4 come first only where the big-cell kernels take
-    them"""
+    model above, with its counts (items, leading items in runs of 4, items in
+    runs); the runs of 4 come first only where the big-cell kernels take them"""
     ids, w = synth.routing(cfg)
     T, K = ids.shape
     p = oracle.plan(ids, w, cfg.E, cfg.tm)
@@ -190,7 +191,7 @@ def test_worklist_layout(cfg, fused, packed):
     R = z.max_rows
     dt = abi.DTYPE_NAME[cfg.dtype]
     first = packed and abi.moe_ffn_big_cells(cfg.E, cfg.d, cfg.f, cfg.tm, R, dt) != 0
-    want, nfour = worklist_model(p["eoff"], cfg.E, R, first)
+    want, nfour, nruns = worklist_model(p["eoff"], cfg.E, R, first)
     say(f"[worklist] {cfg.name} {'forward' if fused else 'expert_ffn'} packed={packed}")
     wts = [torch.zeros((cfg.E, a, b), dtype=TORCH16[cfg.dtype], device="cuda")
            for a, b in ((cfg.d, cfg.f), (cfg.d, cfg.f), (cfg.f, cfg.d))]
@@ -219,5 +220,5 @@ def test_worklist_layout(cfg, fused, packed):
             abi.moe_expert_ffn(xs, *wts, *args)
     torch.cuda.synchronize()
     raw = scratch[: 256 + 16 * len(want)].cpu().numpy().view(np.int32)
-    assert raw[0] == len(want) and raw[1] == nfour
+    assert raw[0] == len(want) and raw[1] == nfour and raw[2] == nruns
     assert np.array_equal(raw[64:].reshape(-1, 4), want)
