@@ -206,21 +206,6 @@ int moe_ffn_splits(int E, int d, int f, int tm, int64_t max_rows, int dtype, int
 int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on);
 
 /*
- * moe_ffn_narrow_cells -- host only: which projections of the packed entry
- * points with fp16 or bf16 run on narrow cells, the small-batch (decode) path
- * (*on bit 0 = gate/up, bit 1 = down): used when the plan bound leaves fewer
- * than 512 workgroups of the general cells (items x column groups); each
- * wavefront then streams one 16-column fragment of the packed weights over
- * the whole reduction, unsplit ([P3] s.1: the per-(token, expert) job of a
- * decode step). The results are the same bits as the general cells unsplit;
- * the row-major entry points split the reduction instead in that regime
- * (moe_ffn_splits), so packed and row-major results may differ there in
- * rounding (both within the tolerance). Same argument checks as
- * moe_ffn_scratch_bytes.
- */
-int moe_ffn_narrow_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on);
-
-/*
  * moe_expert_ffn -- the grouped expert FFN over the expert-sorted rows
  * ([P3] s.1: gate/up projection, gated activation, weighted down projection
  * per job; [P1] s.1 finding 5 names the SwiGLU and down-projection epilogue

@@ -63,7 +63,6 @@ _SIGS = {
     "moe_ffn_splits": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int),
                        ctypes.POINTER(ctypes.c_int)],
     "moe_ffn_big_cells": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int)],
-    "moe_ffn_narrow_cells": [I32, I32, I32, I32, I64, I32, ctypes.POINTER(ctypes.c_int)],
     "moe_expert_ffn": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ, P],
     "moe_combine": [P, I64, P, I32, I32, I32, P, P],
     "moe_forward_workspace": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
@@ -155,15 +154,6 @@ def moe_ffn_big_cells(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int
     on = ctypes.c_int()
     _check("moe_ffn_big_cells",
            lib().moe_ffn_big_cells(E, d, f, tm, max_rows, dtype, ctypes.byref(on)))
-    return on.value
-
-
-def moe_ffn_narrow_cells(E: int, d: int, f: int, tm: int, max_rows: int, dtype: int) -> int:
-    """which packed 16-bit projections run on narrow cells (the small-batch path):
-    bit 0 gate/up, bit 1 down"""
-    on = ctypes.c_int()
-    _check("moe_ffn_narrow_cells",
-           lib().moe_ffn_narrow_cells(E, d, f, tm, max_rows, dtype, ctypes.byref(on)))
     return on.value
 
 

@@ -61,7 +61,7 @@ int ffn_check(const void *xs, const void *wg, const void *wu, const void *wd, in
         return MOE_EINVAL;
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
     if (z.blocks_gu > kI32Max || z.blocks_dn > kI32Max || z.blocks_big_gu > kI32Max ||
-        z.blocks_big_dn > kI32Max || z.blocks_narrow_gu > kI32Max || z.blocks_narrow_dn > kI32Max)
+        z.blocks_big_dn > kI32Max)
         return MOE_EINVAL;
     if (scratch_bytes < z.scratch_bytes) return MOE_EINVAL;
     return MOE_OK;
@@ -364,17 +364,6 @@ int moe_ffn_big_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, 
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
     const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
     *on = (z.big_gu ? 1 : 0) | (z.big_dn ? 2 : 0);
-    return MOE_OK;
-}
-
-int moe_ffn_narrow_cells(int E, int d, int f, int tm, int64_t max_rows, int dtype, int *on)
-{
-    if (!on || E < 1 || tm < 1 || max_rows < 1 || max_rows > kI32Max - 1024 || !dtype_ok(dtype) ||
-        d < 8 || f < 8 || d % 8 || f % 8)
-        return MOE_EINVAL;
-    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
-    const moe::FfnShape z = moe::ffn_shape(E, tm, max_rows, d, f, dtype);
-    *on = (z.narrow_gu ? 1 : 0) | (z.narrow_dn ? 2 : 0);
     return MOE_OK;
 }
 

@@ -53,8 +53,6 @@ constexpr int kNpl = 4;                 // columns per lane and B stream
 // output columns per 8-wavefront big-cell workgroup: h columns (gate/up) or y
 // columns (down)
 constexpr int big_cols(bool gateup) { return gateup ? 128 : 256; }
-// output columns per narrow-cell workgroup (one slice of h, one of y)
-constexpr int narrow_cols(bool gateup) { return gateup ? 64 : 128; }
 
 int ffn_rows_per_item() { return kItemRows; }
 
@@ -172,9 +170,6 @@ int group_cols(bool gateup) { return kWavesPerBlock * (gateup ? 16 * kNpl : 32 *
 // projection's 123 cells, each streaming 2.9 MB, take 51 us split 5 ways
 // (3: 54, 4: 52; 6 ways no longer fits one round of workgroups: 61).
 constexpr int64_t kSplitBelowCells = 192;
-// packed 16-bit projections with fewer wide cells than this run on narrow
-// cells (a decode layer: 41 items x 3 (gate/up) or x 6 (down) column groups)
-constexpr int64_t kNarrowBelowCells = 512;
 constexpr int64_t kTargetCells = 512;
 // The 8-wavefront kernel takes the runs of 4 items when the plan bound allows
 // this many rows per expert on average.
@@ -211,16 +206,10 @@ FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype)
     split_for(z.max_items * gs_dn, f, kstep, &z.split_dn, &z.steps_dn);
     z.blocks_gu = (z.max_items * gs_gu * z.split_gu + 7) / 8 * 8;
     z.blocks_dn = (z.max_items * gs_dn * z.split_dn + 7) / 8 * 8;
-    // big cells (packed 16-bit weights, experts with hundreds of rows); narrow
-    // cells (packed 16-bit weights, few rows per expert) when the wide cells
-    // would leave the GPU short of workgroups
+    // big cells (packed 16-bit weights, experts with hundreds of rows)
     const bool big = dtype != 0 && max_rows >= kBigMinRowsPerExpert * (int64_t)E;
     z.big_gu = big && z.split_gu == 1;
     z.big_dn = big && z.split_dn == 1;
-    z.narrow_gu = dtype != 0 && !big && z.max_items * gs_gu < kNarrowBelowCells;
-    z.narrow_dn = dtype != 0 && !big && z.max_items * gs_dn < kNarrowBelowCells;
-    z.blocks_narrow_gu = (z.max_items * ((f + narrow_cols(true) - 1) / narrow_cols(true)) + 7) / 8 * 8;
-    z.blocks_narrow_dn = (z.max_items * ((d + narrow_cols(false) - 1) / narrow_cols(false)) + 7) / 8 * 8;
     z.blocks_big_gu = (ffn_max_quads(max_rows) * ((f + big_cols(true) - 1) / big_cols(true)) + 7) / 8 * 8;
     z.blocks_big_dn = (ffn_max_quads(max_rows) * ((d + big_cols(false) - 1) / big_cols(false)) + 7) / 8 * 8;
     z.plane_gu = max_rows * 2 * (int64_t)f;
@@ -1395,261 +1384,6 @@ __global__ __launch_bounds__(kBigThreads) void k_big(const GemmArgs p,
     }
 }
 
-// ---- narrow cells: small batches (decode), packed 16-bit weights -----------
-// With few work items (a handful of tokens: about one row per expert), the
-// wide cells above leave the GPU short of workgroups, and splitting K costs a
-// reduction. A narrow cell instead gives each wavefront one 16-column MFMA
-// fragment of a packed tile (1 KB per K-step and matrix, contiguous) over the
-// whole K range, with a deep register pipeline: a decode layer's gate/up
-// projection becomes ~1,400 wavefronts each streaming its weights with
-// kNarrowStages steps in flight, and no reduction.
-//  * gate/up: a workgroup of 4 wavefronts = one work item x one 64-column
-//    slice of h; wavefront c computes fragment c (columns 4j + c of the slice)
-//    of W_gate and W_up;
-//  * down: a workgroup of 8 wavefronts = one work item x one 128-column slice
-//    of y (one exponent block of the compact format); wavefront (m, c)
-//    computes fragment c of stream m (columns 64 m + 4j + c);
-//  * A (the item's rows) is loaded by every wavefront for its own MFMAs, only
-//    for rows that hold an entry (pad rows and rows past the item read zeros
-//    without memory traffic);
-//  * each accumulator sees the same MFMA sequence as in an unsplit wide cell,
-//    so the results are the same bits;
-//  * epilogue through LDS: the fragments' outputs are written to a row-major
-//    LDS tile and stored as 16-byte row pieces; the compact y's row maxima are
-//    reduced over the 8 wavefronts of the block in LDS.
-constexpr int narrow_waves(bool gateup) { return gateup ? 4 : 8; }
-// register pipeline depth for NMT m-tiles: a stage holds the B fragments (8
-// VGPRs gate/up, 4 down) and NMT A fragments (4 VGPRs each)
-constexpr int narrow_stages(bool gateup, int nmt)
-{
-    return gateup ? (nmt == 1 ? 12 : nmt == 2 ? 8 : 6) : (nmt == 1 ? 16 : nmt == 2 ? 10 : 8);
-}
-
-template <typename T, bool GATEUP, bool GATHERED, int NMT>
-__device__ __forceinline__ void narrow_cell(const GemmArgs &p, const WorkItem it, int cb,
-                                            char *__restrict__ lds)
-{
-    constexpr int ES = 2;
-    constexpr int KSTEP = 32;
-    constexpr int NMAT = GATEUP ? 2 : 1;
-    constexpr int NW = narrow_waves(GATEUP);
-    constexpr int NC = narrow_cols(GATEUP);
-    constexpr int S = narrow_stages(GATEUP, NMT);
-    const int Kd = p.Kd, N = p.N;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nq = lane & 15, kg = lane >> 4;
-    const int c = wave & 3, m = wave >> 2;  // fragment, stream (down)
-
-    // B: this wavefront's fragment in each K-step's packed tile
-    const PackedGeom z = packed_geom(Kd, N, GATEUP, ES);
-    const int slice = cb;  // of 64 (gate/up) or 128 (down) columns
-    const int g = slice >> 2, w = slice & 3;
-    const bool slice_ok = slice * NC < N;  // workgroup-uniform
-    const size_t gbase = ((size_t)it.expert * z.gs + g) * z.nst * z.step_bytes;
-    const uint32_t grange = slice_ok ? (uint32_t)z.nst * z.step_bytes : 0u;
-    const uint32_t vb = (uint32_t)(w * z.m + (GATEUP ? 0 : m)) * 4096u + (uint32_t)c * 1024u +
-                        (uint32_t)lane * 16u;
-    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(static_cast<const char *>(p.B0) + gbase, grange);
-    const __amdgpu_buffer_rsrc_t rb1 =
-        make_rsrc(static_cast<const char *>(GATEUP ? p.B1 : p.B0) + gbase, grange);
-
-    // A: row 16 mt + nq of the item, K chunk kg; rows without an entry read
-    // zeros (offset past the descriptor's range)
-    __amdgpu_buffer_rsrc_t ra;
-    uint32_t va[NMT];
-    if constexpr (GATHERED) ra = make_rsrc(p.A, (uint32_t)((size_t)p.a_rows * Kd * ES));
-    else
-        ra = make_rsrc(static_cast<const T *>(p.A) + (size_t)it.row0 * Kd,
-                       (uint32_t)((size_t)it.nrows * Kd * ES));
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-        const int rl = 16 * mt + nq;
-        const int t = rl < it.nrows ? p.stok[it.row0 + rl] : -1;
-        if constexpr (GATHERED)
-            va[mt] = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES
-                                                      : 0x80000000u;
-        else
-            va[mt] = t >= 0 ? (uint32_t)rl * (uint32_t)Kd * ES : 0x80000000u;
-    }
-
-    float4_t acc[NMAT][NMT];
-#pragma unroll
-    for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) acc[q][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    struct Stage {
-        uint4 b[NMAT];
-        uint4 a[NMT];
-    };
-    auto load = [&](Stage &st, int s) {
-        const uint32_t o = vb + (uint32_t)s * z.step_bytes;
-        st.b[0] = Ld<16, kNT>::run(rb0, o, 0u);
-        if constexpr (GATEUP) st.b[1] = Ld<16, kNT>::run(rb1, o, 0u);
-        const int ka = s * KSTEP + 8 * kg;
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) st.a[mt] = Ld<16>::run(ra, va[mt] + (uint32_t)ka * ES, 0u);
-    };
-    auto compute = [&](const Stage &st, int s) {
-        // A masked past K at its use (a mask at the load would make the
-        // wavefront wait for the load)
-        const uint32_t am = s * KSTEP + 8 * kg < Kd ? 0xffffffffu : 0u;
-#pragma unroll
-        for (int q = 0; q < NMAT; ++q)
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-                acc[q][mt] = Elt<T>::mfma(mask4(st.a[mt], am), st.b[q], acc[q][mt]);
-    };
-    const int nsteps = z.nst;
-    Stage st[S];
-#pragma unroll
-    for (int j = 0; j < S - 1; ++j) {  // in step order, as in the wide cells
-        load(st[j], j);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int s0 = 0; s0 < nsteps; s0 += S) {
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-            // steps past the end load zeros (past the descriptors' ranges)
-            load(st[(j + S - 1) % S], s0 + j + S - 1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(st[j], s0 + j);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // epilogue: lane (nq, kg) holds rows 16 mt + 4 kg + r of column 4 nq + c
-    // (+ 64 m for down) of the workgroup's NC columns
-    const int colw = 4 * nq + c + 64 * (GATEUP ? 0 : m);  // column within the tile
-    if constexpr (GATEUP) {
-        // h = D(silu(g) * u), every row of the item (pad rows give 0)
-        T *tile = reinterpret_cast<T *>(lds);  // [64 rows][64 columns]
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                tile[(16 * mt + 4 * kg + r) * NC + colw] =
-                    (T)(silu(acc[0][mt][r]) * acc[1][mt][r]);
-        __syncthreads();
-        // 16-byte pieces: 8 per row
-        for (int q = tid; q < 16 * NMT * (NC / 8); q += NW * 64) {
-            const int row = q / (NC / 8), piece = q - row * (NC / 8);
-            const int col = slice * NC + 8 * piece;
-            if (row < it.nrows && col < N)
-                store_nt(reinterpret_cast<uint4 *>(static_cast<T *>(p.out) +
-                                                   ((int64_t)it.row0 + row) * N + col),
-                         *reinterpret_cast<const uint4 *>(tile + row * NC + 8 * piece));
-        }
-    } else {
-        // y = sw * acc on rows that hold an entry
-        float *rw = reinterpret_cast<float *>(lds);          // [64] router weights
-        int *rok = reinterpret_cast<int *>(rw + 64);         // [64] row holds an entry
-        float *mx = reinterpret_cast<float *>(rok + 64);     // [8 waves][64] row maxima
-        char *tile = reinterpret_cast<char *>(mx + NW * 64); // [64 rows][128 columns]
-        if (tid < 64) {
-            const bool real = tid < it.nrows && p.stok[it.row0 + tid] >= 0;
-            rw[tid] = real ? p.sw[it.row0 + tid] : 0.0f;
-            rok[tid] = real;
-        }
-        __syncthreads();
-        const bool compact = p.yexp != nullptr;
-        float v[NMT][4];
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[mt][r] = rw[16 * mt + 4 * kg + r] * acc[0][mt][r];
-            }
-        if (compact) {
-            // this wavefront's maximum of each row over its 16 columns (columns
-            // past N count 0), then over the 8 wavefronts
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float a = slice * NC + colw < N ? __builtin_fabsf(v[mt][r]) : 0.f;
-                    const float M = row16_fmax(a);
-                    if (nq == 0) mx[wave * 64 + 16 * mt + 4 * kg + r] = M;
-                }
-            __syncthreads();
-            int ev[NMT][4];
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * mt + 4 * kg + r;
-                    float M = 0.f;
-#pragma unroll
-                    for (int q = 0; q < NW; ++q) M = __builtin_fmaxf(M, mx[q * 64 + row]);
-                    ev[mt][r] = y16_exponent(M);
-                    reinterpret_cast<_Float16 *>(tile)[row * NC + colw] =
-                        (_Float16)(v[mt][r] * pow2f(ev[mt][r]));
-                }
-            // the block's exponents: one byte per row, by the lanes of wave 0
-            // (lane (kg, nq) holds row 16 (nq >> 2) + 4 kg + (nq & 3))
-            if (wave == 0) {
-                const int rl = 16 * (nq >> 2) + 4 * kg + (nq & 3);
-                store_y16_exponents<NMT>(p.yexp + (int64_t)slice * p.estride, it.row0, ev, rl,
-                                         rl < it.nrows && rok[rl]);
-            }
-            __syncthreads();
-            for (int q = tid; q < 16 * NMT * (NC / 8); q += NW * 64) {
-                const int row = q / (NC / 8), piece = q - row * (NC / 8);
-                const int col = slice * NC + 8 * piece;
-                if (row < it.nrows && rok[row] && col < N)
-                    store_nt(reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.out) +
-                                                       ((int64_t)it.row0 + row) * N + col),
-                             *reinterpret_cast<const uint4 *>(tile + (row * NC + 8 * piece) * 2));
-            }
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    reinterpret_cast<float *>(tile)[(16 * mt + 4 * kg + r) * NC + colw] = v[mt][r];
-            __syncthreads();
-            for (int q = tid; q < 16 * NMT * (NC / 4); q += NW * 64) {
-                const int row = q / (NC / 4), piece = q - row * (NC / 4);
-                const int col = slice * NC + 4 * piece;
-                if (row < it.nrows && rok[row] && col < N)
-                    store_nt(reinterpret_cast<float4 *>(static_cast<float *>(p.out) +
-                                                        ((int64_t)it.row0 + row) * N + col),
-                             *reinterpret_cast<const float4 *>(tile + (row * NC + 4 * piece) * 4));
-            }
-        }
-    }
-}
-
-// LDS of a narrow cell: gate/up a [64][64] tile of D; down the router weights,
-// the row maxima of 8 wavefronts and a [64][128] fp32 tile
-constexpr int narrow_lds_bytes(bool gateup)
-{
-    return gateup ? 64 * 64 * 2 : (64 + 64 + 8 * 64) * 4 + 64 * 128 * 4;
-}
-
-// One workgroup per (work item, column slice), XCD-contiguous.
-template <typename T, bool GATEUP, bool GATHERED>
-__global__ __launch_bounds__(narrow_waves(GATEUP) * 64) void k_narrow(
-    const GemmArgs p, const int32_t *__restrict__ ctl, const WorkItem *__restrict__ items)
-{
-    static_assert(sizeof(T) == 2, "narrow cells: 16-bit element types");
-    __shared__ __attribute__((aligned(16))) char lds[narrow_lds_bytes(GATEUP)];
-    constexpr int NC = narrow_cols(GATEUP);
-    const int ncb = (p.N + NC - 1) / NC;
-    const int nitems = ctl[0];
-    const int lb = xcd_logical_block(nitems * ncb);
-    if (lb < 0) return;  // whole workgroup: no barrier reached
-    const int i = lb / ncb, cb = lb - i * ncb;
-    const WorkItem it = items[i];
-    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: narrow_cell<T, GATEUP, GATHERED, 1>(p, it, cb, lds); break;
-    case 2: narrow_cell<T, GATEUP, GATHERED, 2>(p, it, cb, lds); break;
-    case 3: narrow_cell<T, GATEUP, GATHERED, 3>(p, it, cb, lds); break;
-    default: narrow_cell<T, GATEUP, GATHERED, kMT>(p, it, cb, lds); break;
-    }
-}
-
 // ---- split-K reductions (fixed split order) --------------------------------
 __device__ __forceinline__ int rows_of_plan(const int32_t *meta, int64_t max_rows)
 {
@@ -1864,16 +1598,6 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
     p.N = f;
     const dim3 grid((unsigned)z.blocks_gu);
     if constexpr (PACKED && sizeof(T) == 2) {
-        if (z.narrow_gu) {
-            const dim3 ngrid((unsigned)z.blocks_narrow_gu), nthreads(narrow_waves(true) * 64);
-            if (gathered)
-                hipLaunchKernelGGL((k_narrow<T, true, true>), ngrid, nthreads, 0, s, p,
-                                   ctl_of(scratch), items_of(scratch));
-            else
-                hipLaunchKernelGGL((k_narrow<T, true, false>), ngrid, nthreads, 0, s, p,
-                                   ctl_of(scratch), items_of(scratch));
-            return hipGetLastError();
-        }
         if (z.big_gu && z.blocks_big_gu > 0) {
             p.skip_quads = 1;
             const dim3 bgrid((unsigned)z.blocks_big_gu);
@@ -1920,12 +1644,6 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
         nyb = (d + kY16Block - 1) / kY16Block;
     }
     if constexpr (PACKED && sizeof(T) == 2) {
-        if (z.narrow_dn) {
-            hipLaunchKernelGGL((k_narrow<T, false, false>), dim3((unsigned)z.blocks_narrow_dn),
-                               dim3(narrow_waves(false) * 64), 0, s, p, ctl_of(scratch),
-                               items_of(scratch));
-            return hipGetLastError();
-        }
         if (z.big_dn && z.blocks_big_dn > 0) {
             p.skip_quads = 1;
             hipLaunchKernelGGL((k_big<T, false, false>), dim3((unsigned)z.blocks_big_dn),

@@ -58,11 +58,6 @@ struct FfnShape {
     // blocks)
     bool big_gu, big_dn;
     int64_t blocks_big_gu, blocks_big_dn;
-    // packed 16-bit projections with few work items run on narrow cells (one
-    // 16-column fragment per wavefront, K unsplit): whether, and their grids
-    // (bound on items x column slices)
-    bool narrow_gu, narrow_dn;
-    int64_t blocks_narrow_gu, blocks_narrow_dn;
     int64_t plane_gu, plane_dn;    // floats per partial plane
     size_t part_offset;            // byte offset of the partial planes
     size_t scratch_bytes;

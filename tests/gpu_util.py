@@ -83,29 +83,6 @@ def custom(name, T, d, E, K, f, dtype, tm=16, bias="none", seed=7, x_std=0.02, w
                         x_std=x_std, w_std=w_std)
 
 
-def narrow_bits(cfg) -> int:
-    """which projections of the packed 16-bit layer run on narrow cells (the
-    small-batch path, K unsplit): there the row-major path splits K instead,
-    so packed and row-major results agree within the tolerance, not bit for bit"""
-    if cfg.dtype == "f32":
-        return 0
-    T = cfg.tokens_per_call
-    R = abi.moe_plan_sizes(T, cfg.K, cfg.E, cfg.tm).max_rows
-    return abi.moe_ffn_narrow_cells(cfg.E, cfg.d, cfg.f, cfg.tm, R, abi.DTYPE_NAME[cfg.dtype])
-
-
-def packed_equals_rowmajor(cfg) -> bool:
-    """packed and row-major layers give the same bits unless a projection that the
-    row-major path splits along K runs on narrow cells"""
-    if narrow_bits(cfg) == 0:
-        return True
-    T = cfg.tokens_per_call
-    R = abi.moe_plan_sizes(T, cfg.K, cfg.E, cfg.tm).max_rows
-    sgu, sdn = abi.moe_ffn_splits(cfg.E, cfg.d, cfg.f, cfg.tm, R, abi.DTYPE_NAME[cfg.dtype])
-    nb = narrow_bits(cfg)
-    return not ((nb & 1 and sgu > 1) or (nb & 2 and sdn > 1))
-
-
 def chunk_of(case: Case, c: int):
     """ids, w, x of layer call c (token chunk c)"""
     Tc = case.cfg.tokens_per_call
@@ -114,4 +91,4 @@ def chunk_of(case: Case, c: int):
 
 
 __all__ = ["abi", "synth", "replace", "Case", "make_case", "custom", "dev", "host", "rel_err",
-           "polluted", "say", "TOL", "chunk_of", "narrow_bits", "packed_equals_rowmajor"]
+           "polluted", "say", "TOL", "chunk_of"]

@@ -10,8 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (TOL, abi, custom, dev, host, make_case, narrow_bits, packed_equals_rowmajor,
-                      rel_err, say, synth)
+from gpu_util import TOL, abi, custom, dev, host, make_case, rel_err, say, synth
 from test_gpu_ffn import PATHS as FFN_PATHS
 
 pytestmark = pytest.mark.gpu
@@ -26,13 +25,12 @@ CASES = [
     custom("min_dims_bf16", T=50, d=8, E=4, K=2, f=8, dtype="bf16", x_std=1.0, w_std=0.5),
     custom("k_equals_e_f32", T=20, d=40, E=6, K=6, f=24, dtype="f32", x_std=1.0),
     custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
-] + [c[0] for c in FFN_PATHS] + [
-    # narrow cells (few rows per expert, few work items) whose top expert fills
-    # whole 64-row items (the 4 m-tile variant), ragged d and f
-    custom("narrow_skewed_bf16", T=96, d=328, E=48, K=2, f=200, dtype="bf16",
+    # few work items, skewed: split K on both paths, items of 1 to 4 m-tiles,
+    # ragged d and f
+    custom("few_items_skewed_bf16", T=96, d=328, E=48, K=2, f=200, dtype="bf16",
            bias="zipf1.1", x_std=1.0),
-    custom("narrow_skewed_f16", T=130, d=256, E=64, K=3, f=136, dtype="f16", bias="zipf1.1"),
-]
+    custom("few_items_skewed_f16", T=130, d=256, E=64, K=3, f=136, dtype="f16", bias="zipf1.1"),
+] + [c[0] for c in FFN_PATHS]
 
 # shapes whose packed 16-bit gate/up runs each expert's runs of 4 items on the
 # 8-wavefront kernel (plan bound >= 64 rows per expert, no K split): h columns
@@ -70,12 +68,7 @@ def test_forward_packed_equals_rowmajor(cfg):
     b, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
                        workspace=ws, packed=pk)
     torch.cuda.synchronize()
-    if packed_equals_rowmajor(cfg):
-        assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
-    else:  # narrow cells (K unsplit) against the row-major split: both against the oracle
-        ref = oracle.ffn(case.x, case.ids, case.w, case.wg, case.wu, case.wd, cfg.dtype, True)
-        for out in (a, b):
-            assert rel_err(host(out), ref.astype(np.float32)) <= TOL[cfg.dtype]
+    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
     case.drop_device()
 
 
@@ -135,27 +128,16 @@ def test_expert_ffn_packed_equals_rowmajor(cfg):
                                cfg.E, cfg.d, cfg.f, cfg.tm, *args, h, y, scratch)
         torch.cuda.synchronize()
         outs.append((host(h), host(y)))
-    if packed_equals_rowmajor(cfg):
-        assert np.array_equal(outs[0][0], outs[1][0])
-        assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
-    else:  # narrow cells: h and y of every entry of both paths against the oracle
-        flat = case.ids.reshape(-1)
-        ent = np.nonzero((flat >= 0) & (flat < cfg.E))[0].astype(np.int32)
-        ry, rh = oracle.ffn_entries(case.x, case.ids, case.w, case.wg, case.wu, case.wd,
-                                    cfg.dtype, True, ent)
-        rows = p["pos"][ent]
-        for hh, yy in outs:
-            hv = oracle.decode(hh.view(np.uint16).reshape(R, cfg.f)[rows], cfg.dtype)
-            assert rel_err(hv, rh) <= TOL[cfg.dtype]
-            assert rel_err(yy.reshape(R, cfg.d)[rows], ry) <= TOL[cfg.dtype]
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
     case.drop_device()
 
 
 @pytest.mark.parametrize("name", ["prefill_fp16", "decode_bf16", "ubatch_bf16",
                                   "long_onepass_fp16"])
 def test_forward_packed_full_size(name):
-    """full-size workloads: packed == row-major bitwise (where no narrow cell meets a
-    split projection), and packed vs the oracle on a sample of tokens"""
+    """full-size workloads: packed == row-major bitwise, and packed vs the oracle
+    on a sample of tokens"""
     cfg = synth.CONFIGS[name]
     case = make_case(cfg)
     say(f"[packed forward] {name} full size")
@@ -166,8 +148,7 @@ def test_forward_packed_full_size(name):
     b, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
                        workspace=ws, packed=pk)
     got = host(b)
-    if packed_equals_rowmajor(cfg):
-        assert np.array_equal(got_a.view(np.uint32), got.view(np.uint32))
+    assert np.array_equal(got_a.view(np.uint32), got.view(np.uint32))
     g = np.random.default_rng(cfg.seed)
     toks = np.unique(np.concatenate([[0, cfg.T - 1], g.choice(cfg.T, min(16, cfg.T),
                                                               replace=False)])).astype(np.int32)
@@ -176,22 +157,3 @@ def test_forward_packed_full_size(name):
     assert rel_err(got[toks], ref.astype(np.float32)) <= TOL[cfg.dtype]
     del pk
     case.drop_device()
-
-
-def test_narrow_cases_cover_every_m_tile_count():
-    """the narrow-cell cases above include items of 1 to 4 m-tiles (rows of one
-    expert up to 64 per item) on both projections"""
-    seen = set()
-    for cfg in CASES:
-        if narrow_bits(cfg) != 3:
-            continue
-        ids, _ = synth.routing(cfg)
-        cnt = np.bincount(ids[(ids >= 0) & (ids < cfg.E)].ravel(), minlength=cfg.E)
-        rows = (cnt + cfg.tm - 1) // cfg.tm * cfg.tm
-        for r in rows[rows > 0]:
-            full, rest = divmod(int(r), 64)
-            if full:
-                seen.add(4)
-            if rest:
-                seen.add((rest + 15) // 16)
-    assert seen == {1, 2, 3, 4}, seen

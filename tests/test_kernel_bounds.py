@@ -299,50 +299,3 @@ def test_gather_partition_copies_every_row_once_in_bounds(cfg):
             assert np.all((tt < T))  # tokens read are rows of x (pads read nothing)
             copies[mine] += 1
     assert np.all(copies == 1)
-
-
-def test_narrow_cells_stay_in_bounds():
-    """narrow cells (packed 16-bit weights, small batches): the grid covers every
-    (item, column slice); each wavefront's fragment descriptor lies in the packed
-    weights, its in-step offsets within one K-step; rows and exponent bytes stay
-    inside h, y and the exponent region; the LDS tiles fit"""
-    from gpu_util import narrow_bits
-    cases = [c for c in CASES if narrow_bits(c)]
-    assert cases
-    for cfg in cases:
-        T = cfg.tokens_per_call
-        ids, w = synth.routing(cfg, T)
-        dt = abi.DTYPE_NAME[cfg.dtype]
-        R = abi.moe_plan_sizes(T, cfg.K, cfg.E, cfg.tm).max_rows
-        p, items, _ = plan_items(cfg, T, ids, w, R, False)
-        nb = narrow_bits(cfg)
-        for gateup in (True, False):
-            if not nb & (1 if gateup else 2):
-                continue
-            Kd, N = (cfg.d, cfg.f) if gateup else (cfg.f, cfg.d)
-            NC = 64 if gateup else 128
-            ncb = ceil(N, NC)
-            pg = packed_geom(Kd, N, gateup, 2)
-            B = abi.moe_packed_weight_bytes(cfg.E, cfg.d, cfg.f, dt,
-                                            abi.MOE_W_GATE_UP if gateup else abi.MOE_W_DOWN)
-            grid = round8(max_items(cfg.E, cfg.tm, R) * ncb)
-            assert ceil(len(items) * ncb, 8) <= grid // 8
-            for it in items:
-                ex, row0, nrows, _ = (int(v) for v in it)
-                assert 0 < nrows <= 64 and row0 + nrows <= R
-                for sl in range(ncb):
-                    g, wsl = sl >> 2, sl & 3
-                    assert g < pg["gs"]
-                    gbase = (ex * pg["gs"] + g) * pg["nst"] * pg["step"]
-                    check_range("narrow B", gbase, pg["nst"] * pg["step"], B)
-                    for wave in range(4 if gateup else 8):
-                        c, m = wave & 3, wave >> 2
-                        vb = (wsl * pg["m"] + (0 if gateup else m)) * 4096 + c * 1024 + 63 * 16
-                        assert vb + 16 <= pg["step"]  # one fragment row within a K-step
-                    assert sl * NC < N
-                    for row in range(nrows):
-                        for col in range(sl * NC, min(N, sl * NC + NC), 8):
-                            assert col + 8 <= N
-                        if not gateup:  # exponent byte of block sl, row row0 + row
-                            assert sl * R + row0 + row < ceil(cfg.d, 128) * R
-        assert 64 * 64 * 2 <= 8192 and (64 + 64 + 8 * 64) * 4 + 64 * 128 * 4 <= 64 * 1024
