@@ -205,7 +205,11 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
 // than two extra dependent launches. Each lane issues all its loads of ids
 // at once (at most kFusedMaxBlocks), and its own entry's id and router
 // weight before the counting, so that the placement does not wait for them.
+// One LDS atomic per entry counts it twice: the low 16 bits of s_cnt[e] count
+// all entries of expert e, the high 16 bits those before this block (at most
+// kFusedMaxBlocks * kPlanBlock = 32,768 entries, so neither half overflows).
 constexpr int kFusedMaxBlocks = 32;
+static_assert(kFusedMaxBlocks * kPlanBlock <= 65535, "16-bit halves of the fused counters");
 
 __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int32_t *__restrict__ ids, const float *__restrict__ w, int nent, int E, int K, int tm,
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     int32_t *__restrict__ pos, int32_t *__restrict__ meta, int32_t *__restrict__ ctl,
     WorkItem *__restrict__ items, int max_items, int max_rows, int runs_first)
 {
-    __shared__ int s_tot[kMaxExperts], s_before[kMaxExperts], s_eoff[kMaxExperts];
+    __shared__ int s_cnt[kMaxExperts], s_eoff[kMaxExperts];
     __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
     __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16],
         s_psum[16];
@@ -227,8 +231,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int e = inb ? ids[i] : -1;
     const float wi = inb ? w[i] : 0.0f;
     for (int q = tid; q < E; q += kPlanBlock) {
-        s_tot[q] = 0;
-        s_before[q] = 0;
+        s_cnt[q] = 0;
         wc[q] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
@@ -248,8 +251,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             const int j = i0 + u * kPlanBlock;
             const int ej = v[u];
             if ((unsigned)ej < (unsigned)E) {
-                atomicAdd(&s_tot[ej], 1);
-                if (j < bstart) atomicAdd(&s_before[ej], 1);
+                atomicAdd(&s_cnt[ej], j < bstart ? 0x10001 : 1);
             } else if (j < nent) {
                 skip += (ej == -1);
                 bad += (ej != -1);
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     __syncthreads();
 
     // 2. padded rows and their exclusive scan over experts (lane e = expert e)
-    const int c = tid < E ? s_tot[tid] : 0;
+    const int c = tid < E ? s_cnt[tid] & 0xffff : 0;
     const int rows = (c + tm - 1) / tm * tm;
     const int incl = wave_inclusive_scan(rows, lane);
     const int act = wave_sum(c > 0 ? 1 : 0);
@@ -300,49 +302,44 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int start = before + incl - rows;
     if (tid < E) {
         s_eoff[tid] = start;
-        boff[(size_t)b * E + tid] = s_before[tid];
+        boff[(size_t)b * E + tid] = s_cnt[tid] >> 16;
     }
     {
         // expert tid's layer-wide outputs, by workgroup tid % nblk
         const bool mine = tid < E && tid % (int)gridDim.x == b;
-        if (mine) {
+        if (mine) {  // (its pad rows: after the placement's barrier, below)
             cnt[tid] = c;
             eoff[tid] = start;
-            for (int r = start + c; r < start + rows; ++r) {  // 0..tm-1 pad rows
-                stok[r] = -1;
-                sw[r] = 0.0f;
-            }
         }
         wave_fill_tiles(start / tm, mine ? rows / tm : 0, tid, lane, tiles);
         if (items)  // rows past max_rows (not reached by a plan within its bound) are dropped
             wave_fill_items(mine ? nit : 0, start, rows, qbefore, rbefore, qtotal,
                             runs_first != 0, tid, lane, max_items, max_rows, items);
-        if (b == 0 && tid == 0) {
-            int nact = 0, maxc = 0, nskip = 0, nbad = 0, ptotal = 0;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                ptotal += s_psum[q];
-                nact += s_act[q];
-                maxc = max(maxc, s_max[q]);
-                nskip += s_skip[q];
-                nbad += s_bad[q];
-            }
-            eoff[E] = total;
-            meta[kMetaNent] = nent;
-            meta[kMetaNblk] = gridDim.x;
-            meta[kMetaNr] = total;
-            meta[kMetaNt] = total / tm;
-            meta[kMetaNactive] = nact;
-            meta[kMetaMaxcnt] = maxc;
-            meta[kMetaNskip] = nskip;
-            meta[kMetaNbad] = nbad;
-            meta[kMetaTm] = tm;
-            meta[kMetaE] = E;
-            meta[kMetaK] = K;
-            if (items) {
-                ctl[0] = min(qtotal + rtotal, max_items);
-                ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
-                ctl[2] = min(qtotal + ptotal, max_items);
+        if (b == 0 && wv == 0) {  // the 16 waves' sums, on 16 lanes
+            const bool ql = lane < 16;
+            const int ptotal = wave_sum(ql ? s_psum[lane] : 0);
+            const int nact = wave_sum(ql ? s_act[lane] : 0);
+            const int maxc = wave_max(ql ? s_max[lane] : 0);
+            const int nskip = wave_sum(ql ? s_skip[lane] : 0);
+            const int nbad = wave_sum(ql ? s_bad[lane] : 0);
+            if (lane == 0) {
+                eoff[E] = total;
+                meta[kMetaNent] = nent;
+                meta[kMetaNblk] = gridDim.x;
+                meta[kMetaNr] = total;
+                meta[kMetaNt] = total / tm;
+                meta[kMetaNactive] = nact;
+                meta[kMetaMaxcnt] = maxc;
+                meta[kMetaNskip] = nskip;
+                meta[kMetaNbad] = nbad;
+                meta[kMetaTm] = tm;
+                meta[kMetaE] = E;
+                meta[kMetaK] = K;
+                if (items) {
+                    ctl[0] = min(qtotal + rtotal, max_items);
+                    ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
+                    ctl[2] = min(qtotal + ptotal, max_items);
+                }
             }
         }
     }
@@ -361,12 +358,25 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     if (valid && rank == 0) reinterpret_cast<unsigned char *>(wc)[e * 16 + wv] = (unsigned char)count;
     __syncthreads();
     if (valid) {
-        const int row = s_eoff[e] + s_before[e] + bytes_below(wc[e], wv) + rank;
+        const int row = s_eoff[e] + (s_cnt[e] >> 16) + bytes_below(wc[e], wv) + rank;
         pos[i] = row;
         stok[row] = i / K;
         sw[row] = wi;
     } else if (inb) {
         pos[i] = -1;
+    }
+    // pad rows (token -1, weight +0) of the experts this workgroup owns
+    // (e = b + k nblk): 16 threads per expert write its contiguous pad rows
+    const int nblk = gridDim.x;
+    const int nown = (E - b + nblk - 1) / nblk;
+    for (int k = tid >> 4; k < nown; k += kPlanBlock / 16) {
+        const int ex = b + k * nblk;
+        const int ce = s_cnt[ex] & 0xffff;
+        const int re = (ce + tm - 1) / tm * tm;
+        for (int r = ce + (tid & 15); r < re; r += 16) {
+            stok[s_eoff[ex] + r] = -1;
+            sw[s_eoff[ex] + r] = 0.0f;
+        }
     }
 }
 
