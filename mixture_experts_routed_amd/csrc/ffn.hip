@@ -615,6 +615,10 @@ __device__ __forceinline__ void load_rinfo(const GemmArgs &p, const WorkItem &it
     rinfo[l] = make_float2(WITH_SW && ok ? p.sw[r] : 0.f, __int_as_float(ok ? p.stok[r] : -1));
 }
 
+// Launches with fewer cells than this (the GPU's workgroup slots: 2 per CU)
+// stream their weights deep (see wide_cells)
+constexpr int kDeepBelowCells = 512;
+
 // Pipeline depth of the wide cells for NMT m-tiles: stage = 32 B-operand + 4
 // A-operand VGPRs, accumulators = 32*NMT VGPRs; S stages + accumulators stay
 // <= ~232.
@@ -654,7 +658,10 @@ constexpr int kLdsU4 = 2 * tall_buf_u4(2) > 2 * kATileU4 ? 2 * tall_buf_u4(2) : 
 //    runs' tiles are re-read from L2) the mask moves to the use and the ring
 //    keeps S-1 steps in flight: 7% faster on the down projection of a skewed
 //    2,048-token chunk. Shallow single items beside deep runs in one launch
-//    measured slower than either policy.
+//    measured slower than either policy. A launch of fewer cells than the GPU
+//    holds at once (kDeepBelowCells, two per CU) runs deep too: no other
+//    workgroup shares a CU's memory pipe, so a workgroup's own bytes in flight
+//    set its rate (decode's down projection, 186 cells: 30.3 -> 25.1 us).
 // GATHERED (gate/up only): A is the token activation x [a_rows][Kd] and row r
 // of the item reads x[stok[r]] -- the gather fused into the A-tile loads.
 // The K range is [kb, ke) (a split of the reduction, or all of it).
@@ -1105,8 +1112,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
     const WorkItem it = items[i];
     // weight-stream depth of the launch: deep when at least half the items are
-    // in runs, else shallow (the same for every workgroup)
-    if (2 * ctl[2] >= nitems)
+    // in runs or when the cells do not fill the GPU's workgroup slots, else
+    // shallow (the same for every workgroup)
+    if (2 * ctl[2] >= nitems || (nitems - ifirst) * per_item < kDeepBelowCells)
         gemm_cell<T, GATEUP, GATHERED, PACKED, true>(p, items, it, i, nitems, g, kb, ke, split, lds,
                                                      rinfo);
     else
