@@ -256,6 +256,10 @@ def parse():
                     help="write the calibrated HBM-traffic summary from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run) and exit")
     ap.add_argument("--pmc-command", default="", help="command line recorded in that summary")
+    ap.add_argument("--host-weights", action="store_true",
+                    help="time moe_forward_host_weights (expert weights in pinned host memory, "
+                         "the routed experts staged into a device cache per call) against the "
+                         "device-weight layer on the same inputs, and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a "
                          "kernel of known traffic, to scale hardware byte counters)")
@@ -360,8 +364,96 @@ def cpu_baseline(cfg, ids, w, x, seconds):
                       f"{ntok} tokens ({rows} routed rows), {tt:.1f} s wall"}
 
 
+def host_weights_bench(args):
+    """The layer with its expert weights in pinned host memory: rows/s of
+    moe_forward_host_weights, the device-weight layer on the same inputs, and
+    the staging launch's bytes (the routed experts' three matrices per call)
+    against a plain pinned-to-device copy of the same size."""
+    import torch
+
+    from mixture_experts_routed_amd import abi, synth
+
+    cfg = synth.CONFIGS[args.workload]
+    T, K, E, d, f, tm = cfg.tokens_per_call, cfg.K, cfg.E, cfg.d, cfg.f, cfg.tm
+    dt = abi.DTYPE_NAME[cfg.dtype]
+    tdt = abi.TORCH_DTYPE[dt]
+    ids, w = synth.routing(cfg)
+    x = synth.activations(cfg)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+        return t.view(tdt) if a.dtype == np.uint16 else t
+
+    wts = {k: up(synth.expert_weights(cfg, k)) for k in ("gate", "up", "down")}
+    packed = args.weights == "packed"
+    devw = abi.pack(wts["gate"], wts["up"], wts["down"]) if packed else dict(wts)
+    torch.cuda.synchronize()
+    hostw = {}
+    for k, t in devw.items():  # pinned at allocation, then filled
+        h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        h.copy_(t.cpu())
+        hostw[k] = h
+    xd, idsd, wd = up(x), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    chunks = [(xd[c * T:(c + 1) * T], idsd[c * T:(c + 1) * T], wd[c * T:(c + 1) * T])
+              for c in range(cfg.ncalls)]
+    ws = torch.empty(abi.moe_forward_workspace(T, K, E, d, f, tm, dt), dtype=torch.uint8,
+                     device="cuda")
+    cache = torch.empty(abi.moe_host_cache_bytes(T, K, E, d, f, dt, packed), dtype=torch.uint8,
+                        device="cuda")
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+
+    def host_step():
+        for cx, cids, cw in chunks:
+            abi.moe_forward_host_weights(cx, cids, cw, hostw["gate"], hostw["up"], hostw["down"],
+                                         packed, dt, T, K, E, d, f, tm, cache, ws, out)
+
+    def dev_step():
+        for cx, cids, cw in chunks:
+            abi.forward(cx, cids, cw, wts["gate"], wts["up"], wts["down"], tm=tm, workspace=ws,
+                        out=out, packed=devw if packed else None)
+
+    # bytes staged per step: the three matrices of every routed expert of every call
+    per_expert = sum(t.numel() * t.element_size() for t in devw.values()) // E
+    staged = 0
+    for c in range(cfg.ncalls):
+        cid = ids[c * T:(c + 1) * T]
+        staged += len(np.unique(cid[(cid >= 0) & (cid < E)])) * per_expert
+    host_us = timed_us(host_step, max(1, args.steps))
+    dev_us = timed_us(dev_step, max(1, args.steps))
+    # the host link's plain rate: one pinned-to-device copy of the staged size
+    n = max(staged // cfg.ncalls, 1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    copy_us = timed_us(lambda: dst.copy_(src, non_blocking=True), 5)
+    copy_gbs = n / copy_us / 1e3
+    stage_us = host_us - dev_us
+    line = {
+        "metric": "routed_rows_per_s", "value": T * K * cfg.ncalls / (host_us * 1e-6),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": host_us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "weights": "host (pinned), " +
+                   ("packed" if packed else "row-major")},
+        "host_weights": {
+            "layer_us": round(host_us, 1), "device_weight_layer_us": round(dev_us, 1),
+            "staged_bytes_per_step": staged, "stage_us": round(stage_us, 1),
+            "stage_gbs": round(staged / stage_us / 1e3, 2) if stage_us > 0 else None,
+            "plain_h2d_copy_gbs": round(copy_gbs, 2),
+            "stage_frac_of_copy": round(staged / stage_us / 1e3 / copy_gbs, 3)
+            if stage_us > 0 else None,
+            "note": "stage_us = layer with host weights - layer with device weights, same "
+                    "inputs; the copy is one pinned-to-device transfer of one call's staged "
+                    "bytes through the DMA engines"},
+    }
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
+    if args.host_weights:
+        host_weights_bench(args)
+        return
     if args.pmc_summary:
         rec = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], TRAFFIC_RECORD, args.pmc_command)
         print(json.dumps(rec))

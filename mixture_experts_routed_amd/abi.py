@@ -77,6 +77,9 @@ _SIGS = {
     "moe_expert_ffn_packed": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ,
                               P],
     "moe_forward_packed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P],
+    "moe_host_cache_bytes": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
+    "moe_forward_host_weights": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P, SZ,
+                                 P, SZ, P, P],
     "moe_forward_packed_timed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P,
                                  P],
     "moe_forward_packed_noalloc": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, P],
@@ -114,6 +117,15 @@ def _dev(t, name):
         return None
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _host(t, name):
+    """address of a host tensor (the library checks that it is pinned)"""
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise TypeError(f"{name}: expected a host tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous tensor")
     return t.data_ptr()
@@ -271,6 +283,23 @@ def moe_forward_packed_noalloc(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, 
         _dev(out, "out"), _stream(stream)))
 
 
+def moe_host_cache_bytes(T: int, K: int, E: int, d: int, f: int, dtype: int, packed: bool) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_host_cache_bytes",
+           lib().moe_host_cache_bytes(T, K, E, d, f, dtype, int(packed), ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward_host_weights(x, ids, w, hw_gate, hw_up, hw_down, packed: bool, dtype, T, K, E, d,
+                             f, tm, cache, workspace, out, stream=None):
+    """moe_forward / moe_forward_packed with the expert weights in pinned host tensors."""
+    _check("moe_forward_host_weights", lib().moe_forward_host_weights(
+        _dev(x, "x"), _dev(ids, "ids"), _dev(w, "w"), _host(hw_gate, "hw_gate"),
+        _host(hw_up, "hw_up"), _host(hw_down, "hw_down"), int(packed), dtype, T, K, E, d, f, tm,
+        _dev(cache, "cache"), cache.numel() * cache.element_size(), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _dev(out, "out"), _stream(stream)))
+
+
 class Timer:
     """Per-kernel HIP-event timer of moe_forward_timed."""
 
@@ -358,3 +387,25 @@ def forward(x, ids, w, w_gate, w_up, w_down, tm: int = 16, workspace=None, out=N
         moe_forward(x, ids, w, w_gate, w_up, w_down, dtype, T, K, E, d, f, tm, workspace, out,
                     stream, timer)
     return out, workspace
+
+
+def forward_host(x, ids, w, hw_gate, hw_up, hw_down, tm: int = 16, packed: bool = False,
+                 shapes=None, cache=None, workspace=None, out=None, stream=None):
+    """One routed MoE layer whose expert weights are pinned host tensors (row-major
+    [E, d, f] / [E, f, d], or packed arrays with shapes=(E, d, f)); returns
+    (out, cache, workspace)."""
+    T, d = x.shape
+    K = ids.shape[1]
+    E, _, f = shapes if shapes is not None else hw_gate.shape
+    dtype = DTYPE_OF[x.dtype]
+    need = moe_forward_workspace(T, K, E, d, f, tm, dtype)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cneed = moe_host_cache_bytes(T, K, E, d, f, dtype, packed)
+    if cache is None or cache.numel() < cneed:
+        cache = torch.empty(cneed, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    moe_forward_host_weights(x, ids, w, hw_gate, hw_up, hw_down, packed, dtype, T, K, E, d, f, tm,
+                             cache, workspace, out, stream)
+    return out, cache, workspace

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_routed.so")
-SOURCES = ["route.hip", "plan.hip", "gather_combine.hip", "ffn.hip", "abi.cpp", "noalloc.hip"]
+SOURCES = ["route.hip", "plan.hip", "gather_combine.hip", "ffn.hip", "stage.hip", "abi.cpp",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -254,9 +254,60 @@ int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forwar
     return MOE_OK;
 }
 
+// Expert weights in host memory: the device cache's layout (the slot table,
+// then min(E, T K) slots of each matrix at the layout's per-expert stride).
+struct HostCache {
+    int64_t slots;
+    size_t bgu, bdn;                    // bytes per expert: gate (= up), down
+    size_t slot_of, gate, up, down, total;
+};
+
+int host_cache_layout(int T, int K, int E, int d, int f, int dtype, int packed, HostCache *c)
+{
+    if (T < 1 || K < 1 || K > E || E < 1 || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 ||
+        f % 8 || (packed != 0 && packed != 1) || (int64_t)T * K > kI32Max)
+        return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    const size_t es = elem_bytes(dtype);
+    c->slots = (int64_t)T * K < E ? (int64_t)T * K : E;
+    c->bgu = packed ? moe::packed_weight_bytes(1, d, f, true, dtype) : (size_t)d * f * es;
+    c->bdn = packed ? moe::packed_weight_bytes(1, f, d, false, dtype) : (size_t)f * d * es;
+    auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
+    c->slot_of = 0;
+    c->gate = r256((size_t)E * 4);
+    c->up = r256(c->gate + (size_t)c->slots * c->bgu);
+    c->down = r256(c->up + (size_t)c->slots * c->bgu);
+    c->total = r256(c->down + (size_t)c->slots * c->bdn);
+    return MOE_OK;
+}
+
+// The device address of pinned, device-mapped host memory at p, or nullptr for
+// anything else (pageable host memory, device memory), which the staging
+// kernel must not be given. A failed query's error is cleared here.
+const void *mapped_host(const void *p)
+{
+    if (!p) return nullptr;
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (a.type != hipMemoryTypeHost || !a.devicePointer || !a.hostPointer) return nullptr;
+    return static_cast<const char *>(a.devicePointer) +
+           (static_cast<const char *>(p) - static_cast<const char *>(a.hostPointer));
+}
+
+// Staging of host-resident weights inside a forward call
+struct HostStage {
+    const void *hg, *hu, *hd;  // device addresses of the host weights
+    char *cache;
+    HostCache c;
+};
+
 int forward_impl(const void *x, const int32_t *ids, const float *w, const void *wg, const void *wu,
                  const void *wd, int dtype, int T, int K, int E, int d, int f, int tm, void *ws,
-                 size_t ws_bytes, float *out, hipStream_t s, moe_timer_t *tmr, bool packed = false)
+                 size_t ws_bytes, float *out, hipStream_t s, moe_timer_t *tmr, bool packed = false,
+                 const HostStage *hs = nullptr)
 {
     moe_forward_layout_t L;
     moe_plan_sizes_t z;
@@ -275,6 +326,25 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
                    f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
                    z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items, runs_first(fz, packed));
     if (rc != MOE_OK) return rc;
+    if (hs) {
+        // the routed experts' weights into the cache, the work list to slots
+        if (!items) {
+            if (moe::launch_worklist(i32(L.eoff), E, z.max_rows, b + L.ffn_scratch, fz.max_items,
+                                     runs_first(fz, packed), s) != hipSuccess)
+                return MOE_EHIP;
+            items = true;
+        }
+        char *c = hs->cache;
+        if (moe::launch_stage_experts(i32(L.cnt), E, b + L.ffn_scratch, hs->hg, hs->hu, hs->hd,
+                                      hs->c.bgu, hs->c.bdn, hs->c.slots,
+                                      reinterpret_cast<int32_t *>(c + hs->c.slot_of),
+                                      c + hs->c.gate, c + hs->c.up, c + hs->c.down,
+                                      s) != hipSuccess)
+            return MOE_EHIP;
+        wg = c + hs->c.gate;
+        wu = c + hs->c.up;
+        wd = c + hs->c.down;
+    }
     // The gate/up kernel gathers its rows from x itself when x is addressable
     // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
     const bool fused_gather = (size_t)T * d * elem_bytes(dtype) < ((size_t)1 << 31);
@@ -430,6 +500,41 @@ int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,
 {
     return forward_impl(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, E, d, f, tm, workspace,
                         ws_bytes, out, as_stream(stream), timer, true);
+}
+
+int moe_host_cache_bytes(int T, int K, int E, int d, int f, int dtype, int packed,
+                         size_t *bytes)
+{
+    if (!bytes) return MOE_EINVAL;
+    HostCache c;
+    const int rc = host_cache_layout(T, K, E, d, f, dtype, packed, &c);
+    if (rc == MOE_OK) *bytes = c.total;
+    return rc;
+}
+
+int moe_forward_host_weights(const void *x, const int32_t *ids, const float *w,
+                             const void *w_gate_host, const void *w_up_host,
+                             const void *w_down_host, int packed, int dtype, int T, int K, int E,
+                             int d, int f, int tm, void *cache, size_t cache_bytes,
+                             void *workspace, size_t ws_bytes, float *out, moe_stream_t stream)
+{
+    HostStage hs;
+    int rc = host_cache_layout(T, K, E, d, f, dtype, packed, &hs.c);
+    if (rc != MOE_OK) return rc;
+    if (!cache || !aligned(cache, 256) || cache_bytes < hs.c.total || !w_gate_host ||
+        !w_up_host || !w_down_host || !x || !ids || !w || !workspace || !out)
+        return MOE_EINVAL;
+    hs.hg = mapped_host(w_gate_host);
+    hs.hu = mapped_host(w_up_host);
+    hs.hd = mapped_host(w_down_host);
+    if (!hs.hg || !hs.hu || !hs.hd || !aligned(hs.hg, 16) || !aligned(hs.hu, 16) ||
+        !aligned(hs.hd, 16))
+        return MOE_EINVAL;
+    hs.cache = static_cast<char *>(cache);
+    // the cache's matrices stand in for the device weights (checked as such)
+    return forward_impl(x, ids, w, hs.cache + hs.c.gate, hs.cache + hs.c.up, hs.cache + hs.c.down,
+                        dtype, T, K, E, d, f, tm, workspace, ws_bytes, out, as_stream(stream),
+                        nullptr, packed != 0, &hs);
 }
 
 int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,

@@ -89,4 +89,14 @@ size_t packed_weight_bytes(int E, int Kd, int N, bool gateup, int dtype);
 hipError_t launch_pack(int dtype, const void *src, int E, int Kd, int N, bool gateup, void *dst,
                        hipStream_t s);
 
+// Expert weights in host memory (stage.hip): copy the routed experts' three
+// matrices (bytes_gu per expert for gate and up, bytes_dn for down; hg, hu, hd
+// device-mapped host pointers) into cache slots in ascending expert order,
+// write slot_of[E], and renumber the work list in ffn_scratch to slots.
+// max_slots bounds the routed experts (min(E, T K)).
+hipError_t launch_stage_experts(const int32_t *cnt, int E, const void *ffn_scratch,
+                                const void *hg, const void *hu, const void *hd, size_t bytes_gu,
+                                size_t bytes_dn, int64_t max_slots, int32_t *slot_of, void *cg,
+                                void *cu, void *cd, hipStream_t s);
+
 }  // namespace moe

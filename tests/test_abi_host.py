@@ -177,3 +177,57 @@ def test_noalloc_refuses_requests_beyond_its_buffer_before_any_hip_call():
     assert L.moe_forward_packed_noalloc(A, A, A, A, A, A, abi.MOE_F16, 4, 8, 2000, 2816, 704, 16,
                                         A, None) == 2
     assert abi.moe_status_str(4).startswith("request larger than the fixed buffer")
+
+
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T,K,E,d,f,dtype,packed", [(4, 8, 128, 2816, 704, 2, 1),
+                                                    (64, 2, 8, 128, 256, 0, 0),
+                                                    (96, 2, 48, 328, 200, 1, 1),
+                                                    (3, 2, 1024, 64, 64, 0, 1)])
+def test_host_cache_bytes_closed_form(T, K, E, d, f, dtype, packed):
+    """the expert cache of moe_forward_host_weights: a table of E int32, then
+    min(E, T K) slots of each matrix at the layout's per-expert size, each region
+    at a 256-byte boundary"""
+    L = abi.lib()
+    v = ctypes.c_size_t()
+    es = 4 if dtype == 0 else 2
+    if packed:
+        assert L.moe_packed_weight_bytes(1, d, f, dtype, 0, ctypes.byref(v)) == 0
+        bgu = v.value
+        assert L.moe_packed_weight_bytes(1, d, f, dtype, 1, ctypes.byref(v)) == 0
+        bdn = v.value
+    else:
+        bgu = bdn = d * f * es
+    slots = min(E, T * K)
+    want = r256(r256(r256(r256(E * 4) + slots * bgu) + slots * bgu) + slots * bdn)
+    assert L.moe_host_cache_bytes(T, K, E, d, f, dtype, packed, ctypes.byref(v)) == 0
+    assert v.value == want
+
+
+def test_host_cache_bytes_and_forward_host_weights_reject_bad_arguments():
+    """sizes and buffers are checked before any HIP call (the host pointers are
+    only inspected once everything else is valid)"""
+    L = abi.lib()
+    v = ctypes.c_size_t()
+    assert L.moe_host_cache_bytes(4, 8, 128, 2816, 704, 2, 2, ctypes.byref(v)) == 1  # packed=2
+    assert L.moe_host_cache_bytes(4, 9, 8, 64, 64, 1, 0, ctypes.byref(v)) == 1       # K > E
+    assert L.moe_host_cache_bytes(4, 2, 8, 60, 64, 1, 0, ctypes.byref(v)) == 1       # d % 8
+    assert L.moe_host_cache_bytes(4, 2, 2000, 64, 64, 1, 0, ctypes.byref(v)) == 2    # E too large
+    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, None) == 1
+    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, ctypes.byref(v)) == 0
+    need = v.value
+    A = 1 << 20  # made-up, never dereferenced addresses
+    args = [A, A, A, A, A, A, 0, 1, 4, 2, 8, 64, 64, 16]
+    fwd = L.moe_forward_host_weights
+    assert fwd(*args, A, need - 256, A, 1 << 30, A, None) == 1          # small cache
+    assert fwd(*args, A + 16, need, A, 1 << 30, A, None) == 1           # misaligned cache
+    assert fwd(*args, None, need, A, 1 << 30, A, None) == 1             # no cache
+    bad = list(args)
+    bad[3] = None                                                       # no gate weights
+    assert fwd(*bad, A, need, A, 1 << 30, A, None) == 1
+    bad = list(args)
+    bad[6] = 3                                                          # packed = 3
+    assert fwd(*bad, A, need, A, 1 << 30, A, None) == 1

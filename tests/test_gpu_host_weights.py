@@ -1,0 +1,112 @@
+"""Expert weights in host memory (moe_forward_host_weights): the routed experts'
+matrices are copied from pinned host memory into a device cache in ascending
+expert order and the work list is renumbered to cache slots, so the layer must
+give the same bits as moe_forward / moe_forward_packed on device copies of the
+same weights (that path is itself checked against the oracle in
+test_gpu_forward / test_gpu_packed). Also: the slot table against the oracle's
+plan, a cache reused by calls with other routing, and pageable host memory
+refused before any launch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import abi, custom, dev, host, make_case, say, synth
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    synth.CONFIGS["tiny_fp32"],
+    synth.CONFIGS["decode_bf16"],
+    custom("few_items_skewed_f16", T=130, d=256, E=64, K=3, f=136, dtype="f16", bias="zipf1.1"),
+    custom("ragged_tails_bf16", T=96, d=328, E=12, K=3, f=200, dtype="bf16", x_std=1.0),
+    custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
+    custom("max_experts_f16", T=300, d=64, E=1024, K=8, f=64, dtype="f16"),
+    custom("ragged_tails_f32", T=80, d=136, E=6, K=2, f=72, dtype="f32", x_std=1.0),
+]
+
+
+def pinned(t):
+    """a new pinned host tensor holding t (allocated pinned, then filled)"""
+    out = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    out.copy_(t)
+    return out
+
+
+def host_sets(case, packed):
+    """(device sets, pinned host sets) of the layer's three matrices"""
+    wg, wu, wd = case.d("wg"), case.d("wu"), case.d("wd")
+    if packed:
+        pk = abi.pack(wg, wu, wd)
+        devs = (pk["gate"], pk["up"], pk["down"])
+    else:
+        devs = (wg, wu, wd)
+    torch.cuda.synchronize()
+    return devs, tuple(pinned(t.cpu()) for t in devs)
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_host_weights_equal_device_weights(cfg, packed):
+    case = make_case(cfg)
+    T = cfg.tokens_per_call
+    say(f"[host weights] {cfg.name} packed={packed}")
+    x, ids, w = dev(case.x[:T], cfg.dtype), dev(case.ids[:T]), dev(case.w[:T])
+    devs, hosts = host_sets(case, packed)
+    ref, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                         packed=dict(zip(("gate", "up", "down"), devs)) if packed else None)
+    got, cache, _ = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=packed,
+                                     shapes=(cfg.E, cfg.d, cfg.f))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32))
+    # the slot table: slot s = the s-th expert with entries, ascending; -1 otherwise
+    p = oracle.plan(case.ids[:T], case.w[:T], cfg.E, cfg.tm)
+    cnt = np.asarray(p["cnt"])
+    want = np.full(cfg.E, -1, np.int32)
+    act = np.nonzero(cnt > 0)[0]
+    want[act] = np.arange(len(act), dtype=np.int32)
+    table = host(cache[: 4 * cfg.E]).view(np.int32)
+    assert np.array_equal(table, want)
+    del devs, hosts, cache
+    case.drop_device()
+
+
+def test_one_cache_serves_calls_with_other_routing():
+    """the cache is rewritten by every call: three calls with different routing
+    (the skewed long prompt's first chunks) share one cache and one workspace,
+    each equal to the device-weight layer"""
+    cfg = synth.CONFIGS["long_skewed_fp16"]
+    case = make_case(cfg)
+    T = cfg.tokens_per_call
+    devs, hosts = host_sets(case, True)
+    pk = dict(zip(("gate", "up", "down"), devs))
+    cache = ws = None
+    for c in range(3):
+        sl = slice(c * T, (c + 1) * T)
+        say(f"[host weights] long_skewed chunk {c}")
+        x, ids, w = dev(case.x[sl], cfg.dtype), dev(case.ids[sl]), dev(case.w[sl])
+        ref, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                             packed=pk)
+        got, cache, ws = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=True,
+                                          shapes=(cfg.E, cfg.d, cfg.f), cache=cache, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32)), c
+    del devs, hosts, pk, cache
+    case.drop_device()
+
+
+def test_pageable_host_memory_is_refused():
+    """weights in ordinary (pageable) host memory are refused with MOE_EINVAL
+    before any launch; the output is left untouched"""
+    cfg = synth.CONFIGS["tiny_fp32"]
+    case = make_case(cfg)
+    T = cfg.tokens_per_call
+    x, ids, w = dev(case.x[:T], cfg.dtype), dev(case.ids[:T]), dev(case.w[:T])
+    pageable = tuple(torch.from_numpy(np.ascontiguousarray(a)) for a in (case.wg, case.wu, case.wd))
+    out = torch.full((T, cfg.d), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(abi.MoeError) as e:
+        abi.forward_host(x, ids, w, *pageable, tm=cfg.tm, out=out)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    case.drop_device()
