@@ -335,49 +335,58 @@ int moe_forward_packed(const void *x, const int32_t *ids, const float *w, const 
                        moe_stream_t stream);
 
 /*
- * moe_host_cache_bytes -- host only: the device bytes of the expert cache that
- * moe_forward_host_weights needs for these sizes and weight layout (packed =
- * 1: the tiles of moe_pack_weights; 0: row-major): a slot table of E int32,
- * then min(E, T*K) slots (the most experts one call can route to) of each of
- * the three matrices, each slot one expert's matrix, each region starting at
- * a 256-byte boundary.
+ * Expert weights in host memory, for layers whose experts do not all fit in
+ * device memory ("#372 Prompt path: an MMQ group's experts gathered in one
+ * launch, after one wait, released by one event", description: the routed
+ * experts are streamed into a ring of device slots, ring entries the routing
+ * does not use are skipped; "Add --moe-mode sweep-prefill: streamed expert
+ * supply for CPU mul_mat_id", Mechanism: the used experts in ascending order).
+ * The weights stay in host memory that is pinned and mapped for the device
+ * (hipHostMalloc; torch pin_memory): w_gate_host, w_up_host [E][d][f] and
+ * w_down_host [E][f][d], or the packed arrays of moe_pack_weights (packed = 1).
+ * A device cache holds `slots` experts (each slot one expert's three
+ * matrices) and the state of a ring over the slots.
+ *
+ * moe_host_cache_bytes -- host only: the cache's device bytes for `slots`
+ * slots (0: the fewest that serve a call of T tokens, min(E, T*K)).
  * Errors: MOE_EINVAL / MOE_EUNSUPPORTED as moe_forward_workspace; MOE_EINVAL
- * also for packed other than 0 or 1.
- */
-int moe_host_cache_bytes(int T, int K, int E, int d, int f, int dtype, int packed,
-                         size_t *bytes);
-
-/*
+ * also for packed other than 0 or 1 and for slots (other than 0) below
+ * min(E, T*K) or above E.
+ *
+ * moe_host_cache_init -- mark every slot of a cache empty (one launch on
+ * `stream`). Needed before a cache's first use, and again after the host
+ * weights it has copied change. Errors: MOE_EINVAL for a small or unaligned
+ * cache or bad sizes (1 <= slots <= E).
+ *
  * moe_forward_host_weights -- moe_forward (packed = 0) or moe_forward_packed
- * (packed = 1) with the expert weights in host memory, for layers whose
- * experts do not all fit in device memory ("#372 Prompt path: an MMQ group's
- * experts gathered in one launch, after one wait, released by one event",
- * description: the routed experts are streamed into device slots per call;
- * "Add --moe-mode sweep-prefill: streamed expert supply for CPU mul_mat_id",
- * Mechanism: in ascending expert order).
- * After the plan, one launch copies the three matrices of every expert this
- * call routes to from host memory into `cache` (slot s = the s-th routed
- * expert in ascending order; cache's slot table holds slot_of[e], -1 for the
- * others) and renumbers the work list to slots; the grouped FFN then reads the
- * cache. The GPU reads the host memory itself, so the call enqueues on the
- * stream like moe_forward and never waits for the GPU; its time is that of
- * the host link for the routed experts' bytes.
- * In:  w_gate_host, w_up_host [E][d][f] and w_down_host [E][f][d] (or the
- *      packed arrays of moe_pack_weights), host memory that is pinned and
- *      mapped for the device (hipHostMalloc; torch pin_memory); the rest as
- *      moe_forward.
- * cache: device, 256-byte aligned, >= moe_host_cache_bytes; written by the
- *      call; it may be reused by the next call on the same stream.
+ * (packed = 1) with the weights in host memory. After the plan, one launch
+ * keeps the slot of every routed expert the cache already holds, gives every
+ * other routed expert (ascending) the next slot of the ring that holds no
+ * expert this call routes to (evicting the expert it held), and renumbers the
+ * work list to slots; a second launch copies the newly placed experts'
+ * matrices from host memory, the GPU reading it over the host link. The
+ * grouped FFN then reads the cache. The call enqueues on the stream like
+ * moe_forward and never waits for the GPU. Calls that share a cache must be
+ * ordered (one stream).
+ * In:  the host weights as above; slots as at moe_host_cache_init (>=
+ *      min(E, T*K)); the rest as moe_forward.
+ * cache: device, 256-byte aligned, >= moe_host_cache_bytes for `slots`, made
+ *      by moe_host_cache_init with the same sizes; updated by the call.
  * Out: out [T][d] fp32, the same bits as moe_forward / moe_forward_packed on
- *      device copies of the same weights.
+ *      device copies of the same weights, whatever the cache held.
  * Errors: those of moe_forward; MOE_EINVAL also for a small or unaligned
- *      cache and for weight pointers that are not pinned, device-mapped host
- *      memory (pageable memory is refused before any launch).
+ *      cache, slots below min(E, T*K), and weight pointers that are not
+ *      pinned, device-mapped host memory (pageable memory is refused before
+ *      any launch).
  */
+int moe_host_cache_bytes(int T, int K, int E, int d, int f, int dtype, int packed, int slots,
+                         size_t *bytes);
+int moe_host_cache_init(void *cache, size_t cache_bytes, int E, int d, int f, int dtype,
+                        int packed, int slots, moe_stream_t stream);
 int moe_forward_host_weights(const void *x, const int32_t *ids, const float *w,
                              const void *w_gate_host, const void *w_up_host,
                              const void *w_down_host, int packed, int dtype, int T, int K, int E,
-                             int d, int f, int tm, void *cache, size_t cache_bytes,
+                             int d, int f, int tm, int slots, void *cache, size_t cache_bytes,
                              void *workspace, size_t ws_bytes, float *out, moe_stream_t stream);
 
 /* Byte offsets of moe_forward's intermediates inside the workspace (host only),

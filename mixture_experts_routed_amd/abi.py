@@ -77,9 +77,11 @@ _SIGS = {
     "moe_expert_ffn_packed": [P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, I64, P, P, P, SZ,
                               P],
     "moe_forward_packed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P],
-    "moe_host_cache_bytes": [I32, I32, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)],
-    "moe_forward_host_weights": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P, SZ,
-                                 P, SZ, P, P],
+    "moe_host_cache_bytes": [I32, I32, I32, I32, I32, I32, I32, I32,
+                             ctypes.POINTER(ctypes.c_size_t)],
+    "moe_host_cache_init": [P, SZ, I32, I32, I32, I32, I32, I32, P],
+    "moe_forward_host_weights": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P,
+                                 SZ, P, SZ, P, P],
     "moe_forward_packed_timed": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, P,
                                  P],
     "moe_forward_packed_noalloc": [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P, P],
@@ -283,21 +285,29 @@ def moe_forward_packed_noalloc(x, ids, w, pw_gate, pw_up, pw_down, dtype, T, K, 
         _dev(out, "out"), _stream(stream)))
 
 
-def moe_host_cache_bytes(T: int, K: int, E: int, d: int, f: int, dtype: int, packed: bool) -> int:
+def moe_host_cache_bytes(T: int, K: int, E: int, d: int, f: int, dtype: int, packed: bool,
+                         slots: int = 0) -> int:
     n = ctypes.c_size_t()
-    _check("moe_host_cache_bytes",
-           lib().moe_host_cache_bytes(T, K, E, d, f, dtype, int(packed), ctypes.byref(n)))
+    _check("moe_host_cache_bytes", lib().moe_host_cache_bytes(T, K, E, d, f, dtype, int(packed),
+                                                              slots, ctypes.byref(n)))
     return n.value
 
 
+def moe_host_cache_init(cache, E, d, f, dtype, packed: bool, slots: int, stream=None):
+    _check("moe_host_cache_init", lib().moe_host_cache_init(
+        _dev(cache, "cache"), cache.numel() * cache.element_size(), E, d, f, dtype, int(packed),
+        slots, _stream(stream)))
+
+
 def moe_forward_host_weights(x, ids, w, hw_gate, hw_up, hw_down, packed: bool, dtype, T, K, E, d,
-                             f, tm, cache, workspace, out, stream=None):
+                             f, tm, slots, cache, workspace, out, stream=None):
     """moe_forward / moe_forward_packed with the expert weights in pinned host tensors."""
     _check("moe_forward_host_weights", lib().moe_forward_host_weights(
         _dev(x, "x"), _dev(ids, "ids"), _dev(w, "w"), _host(hw_gate, "hw_gate"),
         _host(hw_up, "hw_up"), _host(hw_down, "hw_down"), int(packed), dtype, T, K, E, d, f, tm,
-        _dev(cache, "cache"), cache.numel() * cache.element_size(), _dev(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _dev(out, "out"), _stream(stream)))
+        slots, _dev(cache, "cache"), cache.numel() * cache.element_size(),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(out, "out"), _stream(stream)))
 
 
 class Timer:
@@ -390,22 +400,26 @@ def forward(x, ids, w, w_gate, w_up, w_down, tm: int = 16, workspace=None, out=N
 
 
 def forward_host(x, ids, w, hw_gate, hw_up, hw_down, tm: int = 16, packed: bool = False,
-                 shapes=None, cache=None, workspace=None, out=None, stream=None):
+                 shapes=None, slots: int = 0, cache=None, workspace=None, out=None, stream=None):
     """One routed MoE layer whose expert weights are pinned host tensors (row-major
-    [E, d, f] / [E, f, d], or packed arrays with shapes=(E, d, f)); returns
-    (out, cache, workspace)."""
+    [E, d, f] / [E, f, d], or packed arrays with shapes=(E, d, f)), through a device
+    cache of `slots` experts (0: the fewest for T tokens); a new cache is made and
+    cleared here, a given one must have been made for the same sizes and slots.
+    Returns (out, cache, workspace)."""
     T, d = x.shape
     K = ids.shape[1]
     E, _, f = shapes if shapes is not None else hw_gate.shape
     dtype = DTYPE_OF[x.dtype]
+    slots = slots or min(E, T * K)
     need = moe_forward_workspace(T, K, E, d, f, tm, dtype)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    cneed = moe_host_cache_bytes(T, K, E, d, f, dtype, packed)
-    if cache is None or cache.numel() < cneed:
-        cache = torch.empty(cneed, dtype=torch.uint8, device=x.device)
+    if cache is None:
+        cache = torch.empty(moe_host_cache_bytes(T, K, E, d, f, dtype, packed, slots),
+                            dtype=torch.uint8, device=x.device)
+        moe_host_cache_init(cache, E, d, f, dtype, packed, slots, stream)
     if out is None:
         out = torch.empty((T, d), dtype=torch.float32, device=x.device)
     moe_forward_host_weights(x, ids, w, hw_gate, hw_up, hw_down, packed, dtype, T, K, E, d, f, tm,
-                             cache, workspace, out, stream)
+                             slots, cache, workspace, out, stream)
     return out, cache, workspace

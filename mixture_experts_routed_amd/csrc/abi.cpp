@@ -254,31 +254,62 @@ int layout_impl(int T, int K, int E, int d, int f, int tm, int dtype, moe_forwar
     return MOE_OK;
 }
 
-// Expert weights in host memory: the device cache's layout (the slot table,
-// then min(E, T K) slots of each matrix at the layout's per-expert stride).
+// Expert weights in host memory: the device cache's layout for S slots (the
+// state: a 256-byte header with the ring hand and the last call's copy count,
+// slot_of[E], exp_of[S], copy[S]; then S slots of each matrix at the layout's
+// per-expert stride).
 struct HostCache {
-    int64_t slots;
-    size_t bgu, bdn;                    // bytes per expert: gate (= up), down
-    size_t slot_of, gate, up, down, total;
+    int E, S;
+    size_t bgu, bdn;  // bytes per slot: gate (= up), down
+    size_t hdr, slot_of, exp_of, copy, gate, up, down, total;
 };
 
-int host_cache_layout(int T, int K, int E, int d, int f, int dtype, int packed, HostCache *c)
+int host_cache_layout(int E, int d, int f, int dtype, int packed, int S, HostCache *c)
 {
-    if (T < 1 || K < 1 || K > E || E < 1 || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 ||
-        f % 8 || (packed != 0 && packed != 1) || (int64_t)T * K > kI32Max)
+    if (E < 1 || !dtype_ok(dtype) || d < 8 || f < 8 || d % 8 || f % 8 ||
+        (packed != 0 && packed != 1))
         return MOE_EINVAL;
     if (E > MOE_MAX_EXPERTS) return MOE_EUNSUPPORTED;
+    if (S < 1 || S > E) return MOE_EINVAL;
     const size_t es = elem_bytes(dtype);
-    c->slots = (int64_t)T * K < E ? (int64_t)T * K : E;
+    c->E = E;
+    c->S = S;
     c->bgu = packed ? moe::packed_weight_bytes(1, d, f, true, dtype) : (size_t)d * f * es;
     c->bdn = packed ? moe::packed_weight_bytes(1, f, d, false, dtype) : (size_t)f * d * es;
     auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
-    c->slot_of = 0;
-    c->gate = r256((size_t)E * 4);
-    c->up = r256(c->gate + (size_t)c->slots * c->bgu);
-    c->down = r256(c->up + (size_t)c->slots * c->bgu);
-    c->total = r256(c->down + (size_t)c->slots * c->bdn);
+    c->hdr = 0;
+    c->slot_of = 256;
+    c->exp_of = r256(c->slot_of + (size_t)E * 4);
+    c->copy = r256(c->exp_of + (size_t)S * 4);
+    c->gate = r256(c->copy + (size_t)S * 4);
+    c->up = r256(c->gate + (size_t)S * c->bgu);
+    c->down = r256(c->up + (size_t)S * c->bgu);
+    c->total = r256(c->down + (size_t)S * c->bdn);
     return MOE_OK;
+}
+
+// the fewest slots that hold every expert one call of T tokens, top-K, routes to
+int64_t host_cache_min_slots(int T, int K, int E)
+{
+    return (int64_t)T * K < E ? (int64_t)T * K : E;
+}
+
+moe::CacheState cache_state(const HostCache &c, void *cache)
+{
+    char *b = static_cast<char *>(cache);
+    moe::CacheState st;
+    st.hdr = reinterpret_cast<int32_t *>(b + c.hdr);
+    st.slot_of = reinterpret_cast<int32_t *>(b + c.slot_of);
+    st.exp_of = reinterpret_cast<int32_t *>(b + c.exp_of);
+    st.copy = reinterpret_cast<int32_t *>(b + c.copy);
+    st.gate = b + c.gate;
+    st.up = b + c.up;
+    st.down = b + c.down;
+    st.bytes_gu = c.bgu;
+    st.bytes_dn = c.bdn;
+    st.E = c.E;
+    st.S = c.S;
+    return st;
 }
 
 // The device address of pinned, device-mapped host memory at p, or nullptr for
@@ -300,8 +331,8 @@ const void *mapped_host(const void *p)
 // Staging of host-resident weights inside a forward call
 struct HostStage {
     const void *hg, *hu, *hd;  // device addresses of the host weights
-    char *cache;
-    HostCache c;
+    moe::CacheState st;
+    int64_t max_new;
 };
 
 int forward_impl(const void *x, const int32_t *ids, const float *w, const void *wg, const void *wu,
@@ -334,16 +365,12 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
                 return MOE_EHIP;
             items = true;
         }
-        char *c = hs->cache;
-        if (moe::launch_stage_experts(i32(L.cnt), E, b + L.ffn_scratch, hs->hg, hs->hu, hs->hd,
-                                      hs->c.bgu, hs->c.bdn, hs->c.slots,
-                                      reinterpret_cast<int32_t *>(c + hs->c.slot_of),
-                                      c + hs->c.gate, c + hs->c.up, c + hs->c.down,
-                                      s) != hipSuccess)
+        if (moe::launch_cache_stage(hs->st, i32(L.cnt), b + L.ffn_scratch, hs->hg, hs->hu, hs->hd,
+                                    hs->max_new, s) != hipSuccess)
             return MOE_EHIP;
-        wg = c + hs->c.gate;
-        wu = c + hs->c.up;
-        wd = c + hs->c.down;
+        wg = hs->st.gate;
+        wu = hs->st.up;
+        wd = hs->st.down;
     }
     // The gate/up kernel gathers its rows from x itself when x is addressable
     // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
@@ -502,39 +529,56 @@ int moe_forward_packed_timed(const void *x, const int32_t *ids, const float *w,
                         ws_bytes, out, as_stream(stream), timer, true);
 }
 
-int moe_host_cache_bytes(int T, int K, int E, int d, int f, int dtype, int packed,
+int moe_host_cache_bytes(int T, int K, int E, int d, int f, int dtype, int packed, int slots,
                          size_t *bytes)
 {
-    if (!bytes) return MOE_EINVAL;
+    if (!bytes || T < 1 || K < 1 || K > E || (int64_t)T * K > kI32Max || slots < 0) return MOE_EINVAL;
+    const int64_t smin = host_cache_min_slots(T, K, E);
+    if (slots != 0 && slots < smin) return MOE_EINVAL;
     HostCache c;
-    const int rc = host_cache_layout(T, K, E, d, f, dtype, packed, &c);
+    const int rc = host_cache_layout(E, d, f, dtype, packed, slots ? slots : (int)smin, &c);
     if (rc == MOE_OK) *bytes = c.total;
     return rc;
+}
+
+int moe_host_cache_init(void *cache, size_t cache_bytes, int E, int d, int f, int dtype,
+                        int packed, int slots, moe_stream_t stream)
+{
+    HostCache c;
+    const int rc = host_cache_layout(E, d, f, dtype, packed, slots, &c);
+    if (rc != MOE_OK) return rc;
+    if (!cache || !aligned(cache, 256) || cache_bytes < c.total) return MOE_EINVAL;
+    if (moe::launch_cache_clear(cache_state(c, cache), as_stream(stream)) != hipSuccess)
+        return MOE_EHIP;
+    return MOE_OK;
 }
 
 int moe_forward_host_weights(const void *x, const int32_t *ids, const float *w,
                              const void *w_gate_host, const void *w_up_host,
                              const void *w_down_host, int packed, int dtype, int T, int K, int E,
-                             int d, int f, int tm, void *cache, size_t cache_bytes,
+                             int d, int f, int tm, int slots, void *cache, size_t cache_bytes,
                              void *workspace, size_t ws_bytes, float *out, moe_stream_t stream)
 {
-    HostStage hs;
-    int rc = host_cache_layout(T, K, E, d, f, dtype, packed, &hs.c);
+    if (T < 1 || K < 1 || K > E || (int64_t)T * K > kI32Max) return MOE_EINVAL;
+    HostCache c;
+    int rc = host_cache_layout(E, d, f, dtype, packed, slots, &c);
     if (rc != MOE_OK) return rc;
-    if (!cache || !aligned(cache, 256) || cache_bytes < hs.c.total || !w_gate_host ||
-        !w_up_host || !w_down_host || !x || !ids || !w || !workspace || !out)
+    const int64_t smin = host_cache_min_slots(T, K, E);
+    if (slots < smin || !cache || !aligned(cache, 256) || cache_bytes < c.total ||
+        !w_gate_host || !w_up_host || !w_down_host || !x || !ids || !w || !workspace || !out)
         return MOE_EINVAL;
+    HostStage hs;
     hs.hg = mapped_host(w_gate_host);
     hs.hu = mapped_host(w_up_host);
     hs.hd = mapped_host(w_down_host);
     if (!hs.hg || !hs.hu || !hs.hd || !aligned(hs.hg, 16) || !aligned(hs.hu, 16) ||
         !aligned(hs.hd, 16))
         return MOE_EINVAL;
-    hs.cache = static_cast<char *>(cache);
+    hs.st = cache_state(c, cache);
+    hs.max_new = smin;
     // the cache's matrices stand in for the device weights (checked as such)
-    return forward_impl(x, ids, w, hs.cache + hs.c.gate, hs.cache + hs.c.up, hs.cache + hs.c.down,
-                        dtype, T, K, E, d, f, tm, workspace, ws_bytes, out, as_stream(stream),
-                        nullptr, packed != 0, &hs);
+    return forward_impl(x, ids, w, hs.st.gate, hs.st.up, hs.st.down, dtype, T, K, E, d, f, tm,
+                        workspace, ws_bytes, out, as_stream(stream), nullptr, packed != 0, &hs);
 }
 
 int moe_combine(const float *y, int64_t max_rows, const int32_t *pos, int T, int K, int d,

@@ -89,14 +89,24 @@ size_t packed_weight_bytes(int E, int Kd, int N, bool gateup, int dtype);
 hipError_t launch_pack(int dtype, const void *src, int E, int Kd, int N, bool gateup, void *dst,
                        hipStream_t s);
 
-// Expert weights in host memory (stage.hip): copy the routed experts' three
-// matrices (bytes_gu per expert for gate and up, bytes_dn for down; hg, hu, hd
-// device-mapped host pointers) into cache slots in ascending expert order,
-// write slot_of[E], and renumber the work list in ffn_scratch to slots.
-// max_slots bounds the routed experts (min(E, T K)).
-hipError_t launch_stage_experts(const int32_t *cnt, int E, const void *ffn_scratch,
-                                const void *hg, const void *hu, const void *hd, size_t bytes_gu,
-                                size_t bytes_dn, int64_t max_slots, int32_t *slot_of, void *cg,
-                                void *cu, void *cd, hipStream_t s);
+// Expert weights in host memory (stage.hip): a device cache of S expert slots
+// per matrix (bytes_gu per slot for gate and up, bytes_dn for down) and its
+// state (hdr[2]: ring hand, experts copied by the last call; slot_of[E];
+// exp_of[S]; copy[S]).
+struct CacheState {
+    int32_t *hdr, *slot_of, *exp_of, *copy;
+    void *gate, *up, *down;
+    size_t bytes_gu, bytes_dn;
+    int E, S;
+};
+// an empty cache
+hipError_t launch_cache_clear(const CacheState &c, hipStream_t s);
+// give the routed experts slots (ring order from the hand; resident ones
+// kept), renumber the work list in ffn_scratch to slots, and copy the new
+// experts' matrices from the device-mapped host pointers hg, hu, hd; max_new
+// bounds the experts one call routes to (min(E, T K))
+hipError_t launch_cache_stage(const CacheState &c, const int32_t *cnt, const void *ffn_scratch,
+                              const void *hg, const void *hu, const void *hd, int64_t max_new,
+                              hipStream_t s);
 
 }  // namespace moe

@@ -183,14 +183,15 @@ def r256(v):
     return (v + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("T,K,E,d,f,dtype,packed", [(4, 8, 128, 2816, 704, 2, 1),
-                                                    (64, 2, 8, 128, 256, 0, 0),
-                                                    (96, 2, 48, 328, 200, 1, 1),
-                                                    (3, 2, 1024, 64, 64, 0, 1)])
-def test_host_cache_bytes_closed_form(T, K, E, d, f, dtype, packed):
-    """the expert cache of moe_forward_host_weights: a table of E int32, then
-    min(E, T K) slots of each matrix at the layout's per-expert size, each region
-    at a 256-byte boundary"""
+@pytest.mark.parametrize("T,K,E,d,f,dtype,packed,slots", [(4, 8, 128, 2816, 704, 2, 1, 0),
+                                                          (4, 8, 128, 2816, 704, 2, 1, 64),
+                                                          (64, 2, 8, 128, 256, 0, 0, 0),
+                                                          (96, 2, 48, 328, 200, 1, 1, 48),
+                                                          (3, 2, 1024, 64, 64, 0, 1, 0)])
+def test_host_cache_bytes_closed_form(T, K, E, d, f, dtype, packed, slots):
+    """the expert cache of moe_forward_host_weights: a 256-byte header, slot_of[E],
+    exp_of[S], copy[S], then S slots of each matrix at the layout's per-expert size
+    (S = slots, or min(E, T K) for 0), each region at a 256-byte boundary"""
     L = abi.lib()
     v = ctypes.c_size_t()
     es = 4 if dtype == 0 else 2
@@ -201,33 +202,49 @@ def test_host_cache_bytes_closed_form(T, K, E, d, f, dtype, packed):
         bdn = v.value
     else:
         bgu = bdn = d * f * es
-    slots = min(E, T * K)
-    want = r256(r256(r256(r256(E * 4) + slots * bgu) + slots * bgu) + slots * bdn)
-    assert L.moe_host_cache_bytes(T, K, E, d, f, dtype, packed, ctypes.byref(v)) == 0
+    S = slots or min(E, T * K)
+    off = r256(256 + E * 4)
+    off = r256(off + S * 4)
+    off = r256(off + S * 4)
+    off = r256(off + S * bgu)
+    off = r256(off + S * bgu)
+    want = r256(off + S * bdn)
+    assert L.moe_host_cache_bytes(T, K, E, d, f, dtype, packed, slots, ctypes.byref(v)) == 0
     assert v.value == want
 
 
-def test_host_cache_bytes_and_forward_host_weights_reject_bad_arguments():
-    """sizes and buffers are checked before any HIP call (the host pointers are
-    only inspected once everything else is valid)"""
+def test_host_cache_calls_reject_bad_arguments():
+    """sizes, slots and buffers are checked before any HIP call (the host
+    pointers are only inspected once everything else is valid)"""
     L = abi.lib()
     v = ctypes.c_size_t()
-    assert L.moe_host_cache_bytes(4, 8, 128, 2816, 704, 2, 2, ctypes.byref(v)) == 1  # packed=2
-    assert L.moe_host_cache_bytes(4, 9, 8, 64, 64, 1, 0, ctypes.byref(v)) == 1       # K > E
-    assert L.moe_host_cache_bytes(4, 2, 8, 60, 64, 1, 0, ctypes.byref(v)) == 1       # d % 8
-    assert L.moe_host_cache_bytes(4, 2, 2000, 64, 64, 1, 0, ctypes.byref(v)) == 2    # E too large
-    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, None) == 1
-    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, ctypes.byref(v)) == 0
+    B = ctypes.byref(v)
+    assert L.moe_host_cache_bytes(4, 8, 128, 2816, 704, 2, 2, 0, B) == 1     # packed = 2
+    assert L.moe_host_cache_bytes(4, 9, 8, 64, 64, 1, 0, 0, B) == 1          # K > E
+    assert L.moe_host_cache_bytes(4, 2, 8, 60, 64, 1, 0, 0, B) == 1          # d % 8
+    assert L.moe_host_cache_bytes(4, 2, 2000, 64, 64, 1, 0, 0, B) == 2       # E too large
+    assert L.moe_host_cache_bytes(4, 8, 128, 64, 64, 1, 0, 31, B) == 1       # slots < T K
+    assert L.moe_host_cache_bytes(4, 8, 128, 64, 64, 1, 0, 129, B) == 1      # slots > E
+    assert L.moe_host_cache_bytes(4, 8, 128, 64, 64, 1, 0, -1, B) == 1
+    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, 0, None) == 1
+    assert L.moe_host_cache_bytes(4, 2, 8, 64, 64, 1, 0, 8, B) == 0
     need = v.value
     A = 1 << 20  # made-up, never dereferenced addresses
+    init = L.moe_host_cache_init
+    assert init(A, need - 256, 8, 64, 64, 1, 0, 8, None) == 1                # small cache
+    assert init(A + 16, need, 8, 64, 64, 1, 0, 8, None) == 1                 # misaligned
+    assert init(None, need, 8, 64, 64, 1, 0, 8, None) == 1
+    assert init(A, need, 8, 64, 64, 1, 0, 0, None) == 1                      # slots 0
+    assert init(A, need, 8, 64, 64, 1, 0, 9, None) == 1                      # slots > E
     args = [A, A, A, A, A, A, 0, 1, 4, 2, 8, 64, 64, 16]
     fwd = L.moe_forward_host_weights
-    assert fwd(*args, A, need - 256, A, 1 << 30, A, None) == 1          # small cache
-    assert fwd(*args, A + 16, need, A, 1 << 30, A, None) == 1           # misaligned cache
-    assert fwd(*args, None, need, A, 1 << 30, A, None) == 1             # no cache
+    assert fwd(*args, 8, A, need - 256, A, 1 << 30, A, None) == 1           # small cache
+    assert fwd(*args, 8, A + 16, need, A, 1 << 30, A, None) == 1            # misaligned cache
+    assert fwd(*args, 8, None, need, A, 1 << 30, A, None) == 1              # no cache
+    assert fwd(*args, 7, A, need, A, 1 << 30, A, None) == 1                 # slots < min(E, TK)
     bad = list(args)
-    bad[3] = None                                                       # no gate weights
-    assert fwd(*bad, A, need, A, 1 << 30, A, None) == 1
+    bad[3] = None                                                           # no gate weights
+    assert fwd(*bad, 8, A, need, A, 1 << 30, A, None) == 1
     bad = list(args)
-    bad[6] = 3                                                          # packed = 3
-    assert fwd(*bad, A, need, A, 1 << 30, A, None) == 1
+    bad[6] = 3                                                              # packed = 3
+    assert fwd(*bad, 8, A, need, A, 1 << 30, A, None) == 1

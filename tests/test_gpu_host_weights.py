@@ -1,17 +1,19 @@
-"""Expert weights in host memory (moe_forward_host_weights): the routed experts'
-matrices are copied from pinned host memory into a device cache in ascending
-expert order and the work list is renumbered to cache slots, so the layer must
-give the same bits as moe_forward / moe_forward_packed on device copies of the
-same weights (that path is itself checked against the oracle in
-test_gpu_forward / test_gpu_packed). Also: the slot table against the oracle's
-plan, a cache reused by calls with other routing, and pageable host memory
-refused before any launch."""
+"""Expert weights in host memory (moe_forward_host_weights): the routed experts
+are given slots of a device cache (a ring over the slots: resident experts
+keep theirs, new ones take the next free slots from the hand, in ascending
+expert order), the new ones' matrices are copied from pinned host memory, and
+the work list is renumbered to slots. So the layer must give the same bits as
+moe_forward / moe_forward_packed on device copies of the same weights (that
+path is itself checked against the oracle in test_gpu_forward /
+test_gpu_packed), whatever the cache held. Also: the cache state after every
+call of a sequence against a model of the ring, a cache reused by calls with
+other routing, and pageable host memory refused before any launch."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import abi, custom, dev, host, make_case, say, synth
+from gpu_util import abi, custom, dev, host, make_case, replace, say, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -65,9 +67,76 @@ def test_host_weights_equal_device_weights(cfg, packed):
     want = np.full(cfg.E, -1, np.int32)
     act = np.nonzero(cnt > 0)[0]
     want[act] = np.arange(len(act), dtype=np.int32)
-    table = host(cache[: 4 * cfg.E]).view(np.int32)
+    table = host(cache[256: 256 + 4 * cfg.E]).view(np.int32)
     assert np.array_equal(table, want)
     del devs, hosts, cache
+    case.drop_device()
+
+
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+def ring_model(slot_of, exp_of, hand, routed, S):
+    """one call of the cache ring: routed experts (ascending) without a slot take
+    the free slots (those not holding an expert this call routes to) in ring
+    order from the hand, evicting what they held; returns (hand, copies)"""
+    rset = set(routed)
+    new = [e for e in routed if slot_of[e] < 0]
+    free = [(hand + q) % S for q in range(S)
+            if not (exp_of[(hand + q) % S] >= 0 and exp_of[(hand + q) % S] in rset)]
+    copies = []
+    for r, e in enumerate(new):
+        sl = free[r]
+        if exp_of[sl] >= 0:
+            slot_of[exp_of[sl]] = -1
+        slot_of[e] = sl
+        exp_of[sl] = e
+        copies.append((sl, e))
+    if new:
+        hand = (free[len(new) - 1] + 1) % S
+    return hand, copies
+
+
+@pytest.mark.parametrize("slots", [32, 48, 128])
+def test_cache_ring_state_and_outputs_over_a_sequence(slots):
+    """eight decode calls (4 tokens, top-8 of 128 experts) with different routing
+    through one cache of `slots` slots: after every call the hand, the number of
+    experts copied, slot_of and exp_of equal the ring model, and the output equals
+    the device-weight layer bit for bit"""
+    cfg = replace(synth.CONFIGS["decode_bf16"], T=32, chunk=4)
+    case = make_case(cfg)
+    T, E = cfg.tokens_per_call, cfg.E
+    devs, hosts = host_sets(case, True)
+    pk = dict(zip(("gate", "up", "down"), devs))
+    slot_of, exp_of, hand = [-1] * E, [-1] * slots, 0
+    cache = ws = None
+    off_exp = r256(256 + 4 * E)
+    copied = 0
+    for c in range(cfg.ncalls):
+        sl = slice(c * T, (c + 1) * T)
+        x, ids, w = dev(case.x[sl], cfg.dtype), dev(case.ids[sl]), dev(case.w[sl])
+        ref, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                             packed=pk)
+        got, cache, ws = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=True,
+                                          shapes=(E, cfg.d, cfg.f), slots=slots, cache=cache,
+                                          workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32)), c
+        cid = case.ids[sl]
+        routed = sorted(set(int(e) for e in cid.ravel() if 0 <= e < E))
+        hand, copies = ring_model(slot_of, exp_of, hand, routed, slots)
+        copied += len(copies)
+        hdr = host(cache[:8]).view(np.int32)
+        assert (int(hdr[0]), int(hdr[1])) == (hand, len(copies)), c
+        assert np.array_equal(host(cache[256: 256 + 4 * E]).view(np.int32), np.array(slot_of))
+        assert np.array_equal(host(cache[off_exp: off_exp + 4 * slots]).view(np.int32),
+                              np.array(exp_of))
+    # a cache of every expert copies each routed expert once; smaller ones may
+    # copy some again after evicting them
+    nrouted = len(set(int(e) for e in case.ids.ravel() if 0 <= e < E))
+    assert copied >= nrouted and (slots < E or copied == nrouted)
+    del devs, hosts, pk, cache
     case.drop_device()
 
 
