@@ -199,12 +199,15 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
 // for the other workgroups; then it places its own entries exactly as k_place
 // does. The per-expert layer-wide outputs (cnt, eoff, pad rows, tiles and,
 // when asked, the grouped FFN's work items) of expert e are written by
-// workgroup e % nblk, so that no workgroup carries them all; workgroup 0
-// writes eoff[E], meta and the item count. The redundant counting costs
+// workgroup e % nblk, so that no workgroup carries them all; the last
+// wavefront of workgroup 0 writes eoff[E], meta and the item counts at the
+// end, beside the other wavefronts' pad rows. The redundant counting costs
 // nblk * nent LDS atomics in total (20 x 20,480 at T=2048, top-10), far less
 // than two extra dependent launches. Each lane issues all its loads of ids
 // at once (at most kFusedMaxBlocks), and its own entry's id and router
-// weight before the counting, so that the placement does not wait for them.
+// weight, before it clears the counters, so that neither the counting nor the
+// placement waits for more than one load latency. The waves' partial sums are
+// combined by wavefront scans on 16 lanes (one LDS read per array).
 // One LDS atomic per entry counts it twice: the low 16 bits of s_cnt[e] count
 // all entries of expert e, the high 16 bits those before this block (at most
 // kFusedMaxBlocks * kPlanBlock = 32,768 entries, so neither half overflows).
@@ -218,45 +221,46 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     int32_t *__restrict__ pos, int32_t *__restrict__ meta, int32_t *__restrict__ ctl,
     WorkItem *__restrict__ items, int max_items, int max_rows, int runs_first)
 {
-    __shared__ int s_cnt[kMaxExperts], s_eoff[kMaxExperts];
+    // s_cnt[E]: ids == -1 (skipped entries), s_cnt[E + 1]: other ids outside [0, E)
+    __shared__ int s_cnt[kMaxExperts + 2], s_eoff[kMaxExperts];
     __shared__ uint4 wc[kMaxExperts];  // byte q of wc[e]: entries of expert e in wave q
-    __shared__ int s_sum[16], s_act[16], s_max[16], s_skip[16], s_bad[16], s_qsum[16], s_rsum[16],
-        s_psum[16];
+    __shared__ int s_sum[16], s_act[16], s_max[16], s_qsum[16], s_rsum[16], s_psum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x;
     const int bstart = b * kPlanBlock;
-    // this lane's own entry (placed in step 3)
+    // this lane's own entry (placed in step 3), and the entries it counts:
+    // entry tid + u * kPlanBlock for every block u (nent <= U * kPlanBlock),
+    // all loads issued before the counters are cleared. A wavefront whose
+    // entries of block u all lie past nent skips that load; a lane past nent
+    // in a wavefront that loads reads the last entry and does not count it.
     const int i = bstart + tid;
     const bool inb = i < nent;
     const int e = inb ? ids[i] : -1;
     const float wi = inb ? w[i] : 0.0f;
+    constexpr int U = kFusedMaxBlocks;
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        v[u] = -1;
+        if ((tid & ~(kWave - 1)) + u * kPlanBlock < nent)  // wave-uniform
+            v[u] = ids[min(tid + u * kPlanBlock, nent - 1)];
+    }
     for (int q = tid; q < E; q += kPlanBlock) {
         s_cnt[q] = 0;
         wc[q] = make_uint4(0u, 0u, 0u, 0u);
     }
+    if (tid < 2) s_cnt[E + tid] = 0;
     __syncthreads();
 
-    // 1. histogram of all entries, and of the entries before this block
-    int skip = 0, bad = 0;
-    constexpr int U = kFusedMaxBlocks;  // every load of the lane in flight before its atomics
-    for (int i0 = tid; i0 < nent; i0 += U * kPlanBlock) {
-        int v[U];
+    // 1. histogram of all entries, and of the entries before this block (ids
+    // outside [0, E) into the two counters past the experts')
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = i0 + u * kPlanBlock;
-            v[u] = j < nent ? ids[j] : -2;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = i0 + u * kPlanBlock;
-            const int ej = v[u];
-            if ((unsigned)ej < (unsigned)E) {
-                atomicAdd(&s_cnt[ej], j < bstart ? 0x10001 : 1);
-            } else if (j < nent) {
-                skip += (ej == -1);
-                bad += (ej != -1);
-            }
-        }
+    for (int u = 0; u < U; ++u) {
+        const int j = tid + u * kPlanBlock;
+        const int ej = v[u];
+        if (j < nent)
+            atomicAdd(&s_cnt[(unsigned)ej < (unsigned)E ? ej : (ej == -1 ? E : E + 1)],
+                      j < bstart ? 0x10001 : 1);
     }
     __syncthreads();
 
@@ -266,8 +270,6 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int incl = wave_inclusive_scan(rows, lane);
     const int act = wave_sum(c > 0 ? 1 : 0);
     const int mx = wave_max(c);
-    skip = wave_sum(skip);
-    bad = wave_sum(bad);
     // work items of this expert, in runs of 4 and not (only needed by workgroup 0)
     const int nit = (rows + kItemRows - 1) / kItemRows;
     const int nit4 = nit & ~3;
@@ -282,23 +284,22 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     if (lane == 0) {
         s_act[wv] = act;
         s_max[wv] = mx;
-        s_skip[wv] = skip;
-        s_bad[wv] = bad;
         s_psum[wv] = pairs;
     }
     __syncthreads();
-    int before = 0, total = 0, qbefore = qincl - nit4, rbefore = rincl - (nit - nit4);
-    int qtotal = 0, rtotal = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int v = s_sum[q];
-        before += (q < wv) ? v : 0;
-        total += v;
-        qbefore += (q < wv) ? s_qsum[q] : 0;
-        rbefore += (q < wv) ? s_rsum[q] : 0;
-        qtotal += s_qsum[q];
-        rtotal += s_rsum[q];
-    }
+    // the 16 waves' sums, scanned on lanes 0..15 of every wavefront; wave wv
+    // takes the sums of the waves before it from lane wv - 1
+    const int ql = lane & 15;
+    const int cs = wave_inclusive_scan(lane < 16 ? s_sum[ql] : 0, lane);
+    const int cq = wave_inclusive_scan(lane < 16 ? s_qsum[ql] : 0, lane);
+    const int cr = wave_inclusive_scan(lane < 16 ? s_rsum[ql] : 0, lane);
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int total = __builtin_amdgcn_readlane(cs, 15);
+    const int qtotal = __builtin_amdgcn_readlane(cq, 15);
+    const int rtotal = __builtin_amdgcn_readlane(cr, 15);
+    const int before = wvu ? __builtin_amdgcn_readlane(cs, wvu - 1) : 0;
+    const int qbefore = qincl - nit4 + (wvu ? __builtin_amdgcn_readlane(cq, wvu - 1) : 0);
+    const int rbefore = rincl - (nit - nit4) + (wvu ? __builtin_amdgcn_readlane(cr, wvu - 1) : 0);
     const int start = before + incl - rows;
     if (tid < E) {
         s_eoff[tid] = start;
@@ -315,33 +316,6 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         if (items)  // rows past max_rows (not reached by a plan within its bound) are dropped
             wave_fill_items(mine ? nit : 0, start, rows, qbefore, rbefore, qtotal,
                             runs_first != 0, tid, lane, max_items, max_rows, items);
-        if (b == 0 && wv == 0) {  // the 16 waves' sums, on 16 lanes
-            const bool ql = lane < 16;
-            const int ptotal = wave_sum(ql ? s_psum[lane] : 0);
-            const int nact = wave_sum(ql ? s_act[lane] : 0);
-            const int maxc = wave_max(ql ? s_max[lane] : 0);
-            const int nskip = wave_sum(ql ? s_skip[lane] : 0);
-            const int nbad = wave_sum(ql ? s_bad[lane] : 0);
-            if (lane == 0) {
-                eoff[E] = total;
-                meta[kMetaNent] = nent;
-                meta[kMetaNblk] = gridDim.x;
-                meta[kMetaNr] = total;
-                meta[kMetaNt] = total / tm;
-                meta[kMetaNactive] = nact;
-                meta[kMetaMaxcnt] = maxc;
-                meta[kMetaNskip] = nskip;
-                meta[kMetaNbad] = nbad;
-                meta[kMetaTm] = tm;
-                meta[kMetaE] = E;
-                meta[kMetaK] = K;
-                if (items) {
-                    ctl[0] = min(qtotal + rtotal, max_items);
-                    ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
-                    ctl[2] = min(qtotal + ptotal, max_items);
-                }
-            }
-        }
     }
 
     // 3. placement of this block's entries (as k_place, offsets from LDS)
@@ -376,6 +350,35 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         for (int r = ce + (tid & 15); r < re; r += 16) {
             stok[s_eoff[ex] + r] = -1;
             sw[s_eoff[ex] + r] = 0.0f;
+        }
+    }
+    // the layer-wide counts (meta, eoff[E], the work list's item counts), by
+    // the last wavefront of workgroup 0, off the placement's critical path
+    if (b == 0 && wv == kPlanBlock / kWave - 1) {
+        const bool l16 = lane < 16;  // the 16 waves' sums, on 16 lanes
+        const int ptotal = wave_sum(l16 ? s_psum[lane & 15] : 0);
+        const int nact = wave_sum(l16 ? s_act[lane & 15] : 0);
+        const int maxc = wave_max(l16 ? s_max[lane & 15] : 0);
+        const int nskip = s_cnt[E] & 0xffff;
+        const int nbad = s_cnt[E + 1] & 0xffff;
+        if (lane == 0) {
+            eoff[E] = total;
+            meta[kMetaNent] = nent;
+            meta[kMetaNblk] = gridDim.x;
+            meta[kMetaNr] = total;
+            meta[kMetaNt] = total / tm;
+            meta[kMetaNactive] = nact;
+            meta[kMetaMaxcnt] = maxc;
+            meta[kMetaNskip] = nskip;
+            meta[kMetaNbad] = nbad;
+            meta[kMetaTm] = tm;
+            meta[kMetaE] = E;
+            meta[kMetaK] = K;
+            if (items) {
+                ctl[0] = min(qtotal + rtotal, max_items);
+                ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
+                ctl[2] = min(qtotal + ptotal, max_items);
+            }
         }
     }
 }
