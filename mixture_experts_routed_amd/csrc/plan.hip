@@ -211,6 +211,17 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
 // One LDS atomic per entry counts it twice: the low 16 bits of s_cnt[e] count
 // all entries of expert e, the high 16 bits those before this block (at most
 // kFusedMaxBlocks * kPlanBlock = 32,768 entries, so neither half overflows).
+// A workgroup barrier for LDS traffic only: this wavefront's LDS operations
+// complete, then s_barrier. __syncthreads()'s release fence would also wait
+// for every global store in flight (a memory round trip), which nothing in
+// the plan reads back before the kernel ends. As inline asm with a memory
+// clobber, so that the compiler moves no LDS access across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
+    asm volatile("s_barrier" ::: "memory");
+}
+
 constexpr int kFusedMaxBlocks = 32;
 static_assert(kFusedMaxBlocks * kPlanBlock <= 65535, "16-bit halves of the fused counters");
 
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         wc[q] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (tid < 2) s_cnt[E + tid] = 0;
-    __syncthreads();
+    lds_barrier();
 
     // 1. histogram of all entries, and of the entries before this block (ids
     // outside [0, E) into the two counters past the experts')
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
             atomicAdd(&s_cnt[(unsigned)ej < (unsigned)E ? ej : (ej == -1 ? E : E + 1)],
                       j < bstart ? 0x10001 : 1);
     }
-    __syncthreads();
+    lds_barrier();
 
     // 2. padded rows and their exclusive scan over experts (lane e = expert e)
     const int c = tid < E ? s_cnt[tid] & 0xffff : 0;
@@ -286,7 +297,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
         s_max[wv] = mx;
         s_psum[wv] = pairs;
     }
-    __syncthreads();
+    lds_barrier();
     // the 16 waves' sums, scanned on lanes 0..15 of every wavefront; wave wv
     // takes the sums of the waves before it from lane wv - 1
     const int ql = lane & 15;
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
     const int rank = __popcll(same & below);
     const int count = __popcll(same);
     if (valid && rank == 0) reinterpret_cast<unsigned char *>(wc)[e * 16 + wv] = (unsigned char)count;
-    __syncthreads();
+    lds_barrier();
     if (valid) {
         const int row = s_eoff[e] + (s_cnt[e] >> 16) + bytes_below(wc[e], wv) + rank;
         pos[i] = row;
