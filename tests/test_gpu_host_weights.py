@@ -25,6 +25,8 @@ CASES = [
     custom("tm48_f16", T=200, d=96, E=16, K=3, f=80, dtype="f16", tm=48),
     custom("max_experts_f16", T=300, d=64, E=1024, K=8, f=64, dtype="f16"),
     custom("ragged_tails_f32", T=80, d=136, E=6, K=2, f=72, dtype="f32", x_std=1.0),
+    # skipped slots (id -1): their experts need no slot unless another entry routes there
+    replace(custom("tail_skip_f16", T=96, d=256, E=32, K=4, f=128, dtype="f16"), tail_skip=0.75),
 ]
 
 
