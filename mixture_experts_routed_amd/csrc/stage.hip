@@ -51,7 +51,10 @@ __global__ __launch_bounds__(kAssignBlock) void k_cache_assign(
     // the state before the call (every read of exp_of before the first barrier)
     const int hand = hdr[0];
     const bool routed = tid < E && cnt[tid] > 0;
-    const int old_slot = tid < E ? slot_of[tid] : -1;
+    // (a slot number outside [0, S) -- a cache made for other sizes -- counts as
+    // none, so that no work item can address past the cache)
+    const int raw_slot = tid < E ? slot_of[tid] : -1;
+    const int old_slot = (unsigned)raw_slot < (unsigned)S ? raw_slot : -1;
     const int isnew = routed && old_slot < 0 ? 1 : 0;
     const int sq = tid < S ? (hand + tid) % S : 0;
     const int sq_exp = tid < S ? exp_of[sq] : -1;
