@@ -38,9 +38,13 @@ __device__ __forceinline__ float4 load_nt(const float4 *p)
 // round robin). Each row has exactly one owner whatever the placement; only
 // the L2 reuse depends on it. A wavefront copies its matching rows
 // kGatherBatch at a time, with kGatherVec loads per lane and row in flight.
-constexpr int kGatherWaves = 4;
-constexpr int kGatherBatch = 4;
-constexpr int kGatherVec = 4;
+// Small workgroups, one row at a time and 5 vectors per lane (a whole
+// 5,120-byte row per pass at the prefill shape) measured fastest: prefill
+// gather 29.4 us with 4 wavefronts, 4 rows and 4 vectors; 25.4 with 4, 2, 5;
+// 24.2 with 2, 1, 5 (more workgroups in flight, fewer registers each).
+constexpr int kGatherWaves = 2;
+constexpr int kGatherBatch = 1;
+constexpr int kGatherVec = 5;
 
 __global__ __launch_bounds__(kGatherWaves * kWave) void k_gather(
     const uint4 *__restrict__ x, int T, int vpr, const int32_t *__restrict__ stok,

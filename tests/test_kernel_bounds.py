@@ -265,14 +265,26 @@ def test_model_catches_an_undersized_grid():
         model_projection(cfg, None, R, cfg.T, True, True, True, 1, 80, False, short, 0)
 
 
+GATHER_WAVES = 2  # kGatherWaves of the gather kernel
+
+
+def test_gather_model_matches_the_kernel_constant():
+    """the partition model below uses the kernel's workgroup size"""
+    import re
+    from pathlib import Path
+    src = (Path(__file__).resolve().parents[1] / "mixture_experts_routed_amd" / "csrc" /
+           "gather_combine.hip").read_text()
+    assert int(re.search(r"constexpr int kGatherWaves = (\d+);", src).group(1)) == GATHER_WAVES
+
+
 GATHER_CASES = [synth.CONFIGS[n] for n in ("prefill_fp16", "decode_bf16", "tiny_fp32",
                                            "prefill_tailskip_fp16")] + SHAPES[:24]
 
 
 @pytest.mark.parametrize("cfg", GATHER_CASES, ids=[c.name for c in GATHER_CASES])
 def test_gather_partition_copies_every_row_once_in_bounds(cfg):
-    """the standalone gather's grid (row groups of 4 x 64 rows, 8 workgroups per
-    group, one per XCD) and its ownership rule (token mod 8, a pad row by row mod 8)
+    """the standalone gather's grid (row groups of GATHER_WAVES x 64 rows, 8
+    workgroups per group, one per XCD) and its ownership rule (token mod 8, a pad row by row mod 8)
     copy every row below nr exactly once, read only token rows below T and write
     only rows below nr"""
     T = cfg.tokens_per_call
@@ -282,11 +294,11 @@ def test_gather_partition_copies_every_row_once_in_bounds(cfg):
     nr = len(p["stok"])
     stok = np.full(R, -1, np.int64)
     stok[:nr] = p["stok"]
-    blocks = ceil(R, 256) * 8
+    blocks = ceil(R, GATHER_WAVES * 64) * 8
     copies = np.zeros(nr, np.int64)
     for b in range(blocks):
-        for wave in range(4):
-            r0 = ((b >> 3) * 4 + wave) * 64
+        for wave in range(GATHER_WAVES):
+            r0 = ((b >> 3) * GATHER_WAVES + wave) * 64
             if r0 >= nr:
                 continue
             r = np.arange(r0, r0 + 64)
