@@ -102,15 +102,17 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void k_gather(
 // columns of compact rows (Y16: binary16 values, and the exponent e of their
 // 128-column block, block-major: yexp[b * max_rows + row]; each value decoded
 // exactly as s * 2^-e). For a lane's
-// columns, the rows of up to kCombineGroup entries are loaded first -- every
-// load issued, a skipped entry reading row 0 and adding nothing -- then added
-// in k order, so one memory latency covers a group. (Branching around the
-// loads of skipped entries and of slots past K, which are the same for every
-// lane of the workgroup: prefill combine 27.2 -> 26.9 us, but decode 6.7 ->
-// 8.0 us; not kept.)
+// columns, the rows of up to G entries are loaded first -- every load issued,
+// a skipped entry reading row 0 and adding nothing -- then added in k order,
+// so one memory latency covers a group. G is instantiated for 2, 4, 8, 10, 12
+// and 16 and chosen per launch as the smallest that covers min(K, 16): with a
+// fixed G = 16, top-10 lanes loaded 6 rows for nothing (prefill combine 26.9
+// -> 23.0 us, micro-batch 13.6 -> 11.2, decode 6.8 -> 6.1). (Branching around
+// the loads of skipped entries instead, which are the same for every lane of
+// the workgroup: prefill 26.9 us, decode 8.0 us; not kept.)
 constexpr int kCombineGroup = 16;
 
-template <bool Y16>
+template <bool Y16, int G>
 __global__ __launch_bounds__(1024) void k_combine(const void *__restrict__ y,
                                                  const int8_t *__restrict__ yexp,
                                                  int64_t max_rows, int d,
@@ -126,25 +128,25 @@ __global__ __launch_bounds__(1024) void k_combine(const void *__restrict__ y,
         float acc[COLS];
 #pragma unroll
         for (int c = 0; c < COLS; ++c) acc[c] = 0.f;
-        for (int k0 = 0; k0 < K; k0 += kCombineGroup) {
-            const int n = min(kCombineGroup, K - k0);
-            int row[kCombineGroup];
+        for (int k0 = 0; k0 < K; k0 += G) {
+            const int n = min(G, K - k0);
+            int row[G];
 #pragma unroll
-            for (int u = 0; u < kCombineGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int r = u < n ? p[k0 + u] : -1;  // wave-uniform: scalar loads
                 row[u] = (r >= 0 && r < max_rows) ? r : -1;
             }
-            u4 raw[kCombineGroup];
-            int e[kCombineGroup];
+            u4 raw[G];
+            int e[G];
 #pragma unroll
-            for (int u = 0; u < kCombineGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 const int64_t r = row[u] >= 0 ? row[u] : 0;
                 raw[u] = __builtin_nontemporal_load(
                     reinterpret_cast<const u4 *>(y) + r * nvec + j);
                 e[u] = Y16 ? -(int)yexp[(int64_t)((j * COLS) / kY16Block) * max_rows + r] : 0;
             }
 #pragma unroll
-            for (int u = 0; u < kCombineGroup; ++u) {
+            for (int u = 0; u < G; ++u) {
                 if (row[u] < 0) continue;  // wave-uniform
                 // the loaded words as plain values (a bit cast takes values, not
                 // vector elements)
@@ -169,6 +171,31 @@ __global__ __launch_bounds__(1024) void k_combine(const void *__restrict__ y,
     }
 }
 
+// the smallest group size of the instantiated ones that covers min(K, 16)
+// entries, so that no lane loads rows for slots past K
+template <bool Y16>
+void combine_any(int K, dim3 grid, dim3 block, hipStream_t s, const void *y, const int8_t *yexp,
+                 int64_t max_rows, int d, const int32_t *pos, int T, float4 *out)
+{
+    const int g = K < kCombineGroup ? K : kCombineGroup;
+#define MOE_COMBINE(G)                                                                         \
+    hipLaunchKernelGGL((k_combine<Y16, G>), grid, block, 0, s, y, yexp, max_rows, d, pos, T, K, \
+                       out)
+    if (g <= 2)
+        MOE_COMBINE(2);
+    else if (g <= 4)
+        MOE_COMBINE(4);
+    else if (g <= 8)
+        MOE_COMBINE(8);
+    else if (g <= 10)
+        MOE_COMBINE(10);
+    else if (g <= 12)
+        MOE_COMBINE(12);
+    else
+        MOE_COMBINE(kCombineGroup);
+#undef MOE_COMBINE
+}
+
 hipError_t launch_gather(const void *x, int elem_bytes, int T, int d, const int32_t *stok,
                          const int32_t *meta, int64_t max_rows, void *xs, hipStream_t s)
 {
@@ -185,8 +212,8 @@ hipError_t launch_combine(const float *y, int64_t max_rows, const int32_t *pos, 
                           int d, float *out, hipStream_t s)
 {
     const int threads = min(1024, (d / 4 + kWave - 1) / kWave * kWave);
-    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(threads), 0, s, y, nullptr, max_rows, d, pos,
-                       T, K, reinterpret_cast<float4 *>(out));
+    combine_any<false>(K, dim3(T), dim3(threads), s, y, nullptr, max_rows, d, pos, T,
+                       reinterpret_cast<float4 *>(out));
     return hipGetLastError();
 }
 
@@ -194,8 +221,8 @@ hipError_t launch_combine_y16(const uint16_t *y16, const int8_t *yexp, int64_t m
                               const int32_t *pos, int T, int K, int d, float *out, hipStream_t s)
 {
     const int threads = min(1024, (d / 8 + kWave - 1) / kWave * kWave);
-    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(threads), 0, s, y16, yexp, max_rows, d, pos,
-                       T, K, reinterpret_cast<float4 *>(out));
+    combine_any<true>(K, dim3(T), dim3(threads), s, y16, yexp, max_rows, d, pos, T,
+                      reinterpret_cast<float4 *>(out));
     return hipGetLastError();
 }
 
