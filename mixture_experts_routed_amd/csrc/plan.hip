@@ -191,6 +191,17 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
     }
 }
 
+// A workgroup barrier for LDS traffic only: this wavefront's LDS operations
+// complete, then s_barrier. __syncthreads()'s release fence would also wait
+// for every global store in flight (a memory round trip), which nothing in
+// the plan reads back before the kernel ends. As inline asm with a memory
+// clobber, so that the compiler moves no LDS access across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Fused plan for up to kFusedMaxBlocks blocks: one launch instead of three.
 // Each workgroup (block b of 1024 entries) counts every entry of the layer
@@ -211,17 +222,6 @@ __global__ __launch_bounds__(kPlanBlock) void k_place(
 // One LDS atomic per entry counts it twice: the low 16 bits of s_cnt[e] count
 // all entries of expert e, the high 16 bits those before this block (at most
 // kFusedMaxBlocks * kPlanBlock = 32,768 entries, so neither half overflows).
-// A workgroup barrier for LDS traffic only: this wavefront's LDS operations
-// complete, then s_barrier. __syncthreads()'s release fence would also wait
-// for every global store in flight (a memory round trip), which nothing in
-// the plan reads back before the kernel ends. As inline asm with a memory
-// clobber, so that the compiler moves no LDS access across it.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
-    asm volatile("s_barrier" ::: "memory");
-}
-
 constexpr int kFusedMaxBlocks = 32;
 static_assert(kFusedMaxBlocks * kPlanBlock <= 65535, "16-bit halves of the fused counters");
 
