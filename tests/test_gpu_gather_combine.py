@@ -105,13 +105,14 @@ def test_combine_ragged_width():
 
 
 def random_gc(n=30, seed=5151):
-    """seeded random shapes: widths up to 8,192, top-k up to 40 (more than one
-    group of rows loaded together by the combine), tiles 1-32, skipped ids"""
+    """seeded random shapes: widths up to 8,192, top-k up to 40 (every group size
+    the combine is instantiated for -- 2, 4, 8, 10, 12, 16 -- and more than one
+    group of 16), tiles 1-32, skipped ids"""
     g = np.random.default_rng(seed)
     out = []
     for k in range(n):
         E = int(g.choice([1, 3, 16, 64, 300, 1024]))
-        K = int(g.choice([1, 2, 7, 10, 16, 17, 33, 40]))
+        K = int(g.choice([1, 2, 4, 7, 10, 12, 16, 17, 33, 40]))
         T = int(g.choice([1, 3, 64, 500, 2049]))
         d = 8 * int(g.integers(1, 1025))
         d = max(8, min(d, (1 << 25) // (T * K) // 8 * 8))  # expert outputs <= 128 MB
