@@ -173,7 +173,11 @@ def worklist_model(eoff, E, max_rows, runs_first=True):
 
 
 WL = [synth.CONFIGS["prefill_fp16"], custom("wl_skewed", T=3000, d=64, E=24, K=3, f=64,
-                                            dtype="f16", bias="zipf1.1")]
+                                            dtype="f16", bias="zipf1.1"),
+      # at most 64 entries (the one-wavefront plan): decode, and one expert whose 64
+      # rows pad to 96 (a run of 2 items)
+      synth.CONFIGS["decode_bf16"],
+      custom("wl_one_wavefront", T=64, d=64, E=1, K=1, f=64, dtype="f16", tm=48)]
 
 
 @pytest.mark.parametrize("cfg", WL, ids=[c.name for c in WL])

@@ -73,6 +73,12 @@ FUZZ = [
     (4096, 8, 512, 16, 0.02, 0.01, 13),    # 32 blocks: largest single-launch plan
     (32769, 1, 300, 16, 0.0, 0.0, 14),     # 33 blocks: smallest three-launch plan
     (16384, 4, 1000, 8, 0.05, 0.0, 15),    # 64 blocks
+    # at most 64 entries: the one-wavefront plan
+    (8, 8, 1024, 16, 0.1, 0.05, 16),       # 64 entries, E at the limit: 16 experts per lane
+    (64, 1, 1, 48, 0.0, 0.0, 17),          # one expert: 96 padded rows, two work items
+    (4, 16, 16, 1, 0.0, 0.0, 18),          # K = E, duplicates allowed
+    (2, 32, 100, 64, 0.5, 0.0, 19),        # half skipped, tm 64
+    (5, 13, 3, 7, 0.3, 0.3, 20),           # 65 entries: just past one wavefront
 ]
 
 
@@ -101,8 +107,9 @@ def test_plan_bit_exact_fuzz(T, K, E, tm, ps, pb, seed):
     check_plan(ids, w, E, tm, f"fuzz seed {seed}")
 
 
-def test_plan_all_skipped_and_all_bad():
-    T, K, E = 50, 4, 16
+@pytest.mark.parametrize("T", [50, 10], ids=["fused", "one_wavefront"])
+def test_plan_all_skipped_and_all_bad(T):
+    K, E = 4, 16
     ids = np.full((T, K), -1, np.int32)
     w = synth.random_rows(3, T, K)
     g = check_plan(ids, w, E, 16, "all skipped")
