@@ -181,3 +181,51 @@ def test_pageable_host_memory_is_refused():
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
     case.drop_device()
+
+
+def test_host_weights_layer_in_a_graph():
+    """moe_forward_host_weights captured in a HIP graph and replayed: the cache
+    ring is driven by the GPU alone (no memset, no host wait), so three replays
+    with eager work between them equal the device-weight layer, and a replay
+    after new routing is copied into the captured inputs copies the newly
+    routed experts in and equals the device-weight layer on that routing"""
+    cfg = synth.CONFIGS["decode_bf16"]
+    case = make_case(cfg)
+    T, E = cfg.tokens_per_call, cfg.E
+    x, ids, w = dev(case.x[:T], cfg.dtype), dev(case.ids[:T]), dev(case.w[:T])
+    devs, hosts = host_sets(case, True)
+    pk = dict(zip(("gate", "up", "down"), devs))
+    ref, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm, packed=pk)
+    torch.cuda.synchronize()
+    ref_bits = host(ref).view(np.uint32).copy()
+    shapes = (E, cfg.d, cfg.f)
+    _, cache, ws = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=True, shapes=shapes)
+    out = torch.empty_like(ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=True, shapes=shapes, cache=cache,
+                         workspace=ws, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws[: ws.numel() // 2].fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), ref_bits), f"replay {rep}"
+    # new routing: experts the cache does not hold are copied in by the replay
+    g = np.random.default_rng(99)
+    ids2 = np.stack([g.permutation(E)[:cfg.K] for _ in range(T)]).astype(np.int32)
+    ids.copy_(torch.from_numpy(ids2))
+    ref2, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
+                          packed=pk)
+    torch.cuda.synchronize()
+    out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), host(ref2).view(np.uint32))
+    assert int(host(cache[4:8]).view(np.int32)[0]) > 0  # the replay copied experts in
+    del graph, devs, hosts, pk, cache
+    case.drop_device()
