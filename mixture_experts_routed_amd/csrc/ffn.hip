@@ -19,10 +19,10 @@
 //  * Wide cells (an expert with a single item, the common case): the 4
 //    wavefronts share the item's rows (A tile through LDS) and each streams its
 //    own column slice of the weights straight into registers.
-//  * Tall cells (runs of 2 or 4 items of one expert): the wavefronts take
-//    different row blocks of the same column slice(s) and share the weight
-//    tile through LDS, so such an expert's weights are read once per 256
-//    (or 128) rows instead of once per 64 rows.
+//  * Tall cells (runs of 2 items of one expert; a run of 4 is two runs of 2):
+//    the wavefronts take different row blocks of the same column slices and
+//    share the weight tile through LDS, so such an expert's weights are read
+//    once per 128 rows instead of once per 64 rows.
 //  * Split-K when the host-side bound on work items is too small to fill the
 //    256 CUs (decode-sized batches): each split accumulates a K range into an
 //    fp32 partial plane, and a reduce kernel adds the planes in split order
@@ -843,7 +843,8 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
     store_cells<T, GATEUP, NMT>(p, it, col, kg, acc, rinfo, split);
 }
 
-// Tall cells: a run of R (2 or 4) consecutive items of one expert. The 4
+// Tall cells: a run of R consecutive items of one expert (R = 2 is dispatched;
+// the R = 4 shape, one column slice over 256 rows, measured slower). The 4
 // wavefronts take row block rb = wave % R (item i0 + rb, 64 rows) and column
 // slice cs = wave / R of the C = 4/R slices of the workgroup, so the C
 // slices' weight tile is loaded once per K-step and shared through LDS by R
@@ -1067,9 +1068,11 @@ __device__ __forceinline__ void gemm_cell(const GemmArgs &p, const WorkItem *__r
                                           float2 *__restrict__ rinfo)
 {
     const int run = it.run & 0xff, j = (it.run >> 8) & 0xff;
+    // a run of 4 is taken as two runs of 2 (4-item cells, one column slice of
+    // 256 rows each: the skewed long prompt's layer 0.8% slower)
     if (run == 4 && j < 4 && i >= j) {
-        tall_cells<T, GATEUP, GATHERED, PACKED, DEEP, 4>(p, items, i - j, nitems, g, j, kb, ke,
-                                                         split, lds, rinfo);
+        tall_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, items, i - (j & 1), nitems, g, j & 1,
+                                                         kb, ke, split, lds, rinfo);
         return;
     }
     if (run == 2 && j < 2 && i >= j) {
