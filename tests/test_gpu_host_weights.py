@@ -100,8 +100,9 @@ def ring_model(slot_of, exp_of, hand, routed, S):
     return hand, copies
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("slots", [32, 48, 128])
-def test_cache_ring_state_and_outputs_over_a_sequence(slots):
+def test_cache_ring_state_and_outputs_over_a_sequence(slots, packed):
     """eight decode calls (4 tokens, top-8 of 128 experts) with different routing
     through one cache of `slots` slots: after every call the hand, the number of
     experts copied, slot_of and exp_of equal the ring model, and the output equals
@@ -109,8 +110,8 @@ def test_cache_ring_state_and_outputs_over_a_sequence(slots):
     cfg = replace(synth.CONFIGS["decode_bf16"], T=32, chunk=4)
     case = make_case(cfg)
     T, E = cfg.tokens_per_call, cfg.E
-    devs, hosts = host_sets(case, True)
-    pk = dict(zip(("gate", "up", "down"), devs))
+    devs, hosts = host_sets(case, packed)
+    pk = dict(zip(("gate", "up", "down"), devs)) if packed else None
     slot_of, exp_of, hand = [-1] * E, [-1] * slots, 0
     cache = ws = None
     off_exp = r256(256 + 4 * E)
@@ -120,7 +121,7 @@ def test_cache_ring_state_and_outputs_over_a_sequence(slots):
         x, ids, w = dev(case.x[sl], cfg.dtype), dev(case.ids[sl]), dev(case.w[sl])
         ref, _ = abi.forward(x, ids, w, case.d("wg"), case.d("wu"), case.d("wd"), tm=cfg.tm,
                              packed=pk)
-        got, cache, ws = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=True,
+        got, cache, ws = abi.forward_host(x, ids, w, *hosts, tm=cfg.tm, packed=packed,
                                           shapes=(E, cfg.d, cfg.f), slots=slots, cache=cache,
                                           workspace=ws)
         torch.cuda.synchronize()
