@@ -67,10 +67,15 @@ __global__ __launch_bounds__(kPlanBlock) void k_scan(
                 run += v[q];
             }
         }
-        for (; b < nblk; ++b) {
-            const int v = bcnt[(size_t)b * E2 + tid];
-            boff[(size_t)b * E + tid] = run;
-            run += v;
+        if (b < nblk) {  // the last < 32 blocks, their loads in flight together too
+            int v[32];
+#pragma unroll
+            for (int q = 0; q < 32; ++q) v[q] = b + q < nblk ? bcnt[(size_t)(b + q) * E2 + tid] : 0;
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                if (b + q < nblk) boff[(size_t)(b + q) * E + tid] = run;
+                run += v[q];
+            }
         }
     }
     // skipped / bad totals: block-wide sums over the two extra columns
