@@ -97,6 +97,35 @@ def stream_read(src, sink, stream=None):
         raise RuntimeError(f"bench_stream_read: status {rc}")
 
 
+def probe_same_bytes(nbytes, dev, launches=8):
+    """The read probe over nbytes (rounded up to 16) in one launch: median
+    microseconds of single launches. Below 512 MiB each launch reads a region of
+    a buffer at least 4x as large (and at least 1 GiB) that the launches before
+    it did not read last, so that the Infinity Cache (256 MB) serves none of it;
+    from 512 MiB on, every launch reads the same region (a sequential read of at
+    least twice the cache's size gets no hits from it), which keeps the working
+    set, and so the address-translation load, that of the kernel compared."""
+    import torch
+
+    nb = max(16, (int(nbytes) + 15) // 16 * 16)
+    nreg = 1 if nb >= 512 << 20 else max(4 * nb, 1 << 30) // nb
+    buf = torch.empty(nreg * nb, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+    ts = []
+    for i in range(2 + launches):
+        src = buf[(i % nreg) * nb: (i % nreg + 1) * nb]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        stream_read(src, sink)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(a.elapsed_time(b) * 1e3)
+    del buf, sink
+    us = float(np.median(ts))
+    return {"bytes": nb, "us": round(us, 2), "gbs": round(nb / us / 1e3, 1)}
+
+
 def gemm_source_hash() -> str:
     import hashlib
 
@@ -713,6 +742,7 @@ def main():
     gu_bytes = gateup_bytes(cfg, meta, T)
     gu_s = gu_us * 1e-6
     achieved = gu_bytes / gu_s / 1e9
+    same_bytes = probe_same_bytes(gu_bytes, dev)
     flops = stage_flops(cfg, meta)
     mfma_peak = MFMA_PEAK_TFLOPS[cfg.dtype]
     # the gate/up launch is bound by the matrix cores when its arithmetic intensity
@@ -733,6 +763,13 @@ def main():
                                             ("" if packed is not None else "_rowmajor"))
                            if cfg.name == "prefill_fp16" else None,
                 "algorithmic_bytes_per_launch": gu_bytes}
+    roof["read_probe_same_bytes"] = dict(
+        same_bytes, launch_frac=round(achieved / same_bytes["gbs"], 3),
+        note="the read probe reading the gate/up launch's algorithmic byte count in one launch "
+             "(a fresh region of a larger buffer each time, so nothing comes from the Infinity "
+             "Cache), median of single launches timed by events; launch_frac = the gate/up "
+             "launch's algorithmic GB/s over the probe's: a plain read of the same bytes in one "
+             "launch, ramp-up and drain included, reaches this rate")
     rows = cfg.T * K
     res = {
         "metric": METRIC, "value": rows / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1,
