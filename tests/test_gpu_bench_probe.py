@@ -22,3 +22,11 @@ def test_stream_read_probe_runs():
         bench.stream_read(src, sink)
         torch.cuda.synchronize()
         assert torch.all(sink == 7)
+
+
+def test_probe_same_bytes_reads_the_asked_byte_count():
+    # rounded up to 16 bytes; below 512 MiB it cycles over fresh regions of 1 GiB
+    print("[probe] same-bytes probe, 1 MiB + 5 bytes", file=sys.stderr, flush=True)
+    r = bench.probe_same_bytes((1 << 20) + 5, torch.device("cuda:0"), launches=3)
+    assert r["bytes"] == (1 << 20) + 16
+    assert r["us"] > 0 and r["gbs"] > 0
