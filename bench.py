@@ -39,7 +39,8 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_RECORD = os.path.join(PROFILES, "prefill_fp16_hbm_traffic.md")
 TIMER_EVERY = 5  # timed steps that also record the gate/up kernel's HIP events
-GEMM_SOURCES = ["mixture_experts_routed_amd/csrc/ffn.hip", "mixture_experts_routed_amd/csrc/common.hpp"]
+GEMM_SOURCES = ["mixture_experts_routed_amd/csrc/ffn.hip", "mixture_experts_routed_amd/csrc/common.hpp",
+                "mixture_experts_routed_amd/csrc/plan_wave.hpp"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -738,6 +739,21 @@ def main():
                     "ms_per_step": ms_rm,
                     "note": "moe_forward with the row-major weights, same inputs and steps"}
     us = {k: 1e3 * v[0] / max(v[1], 1) for k, v in st_all.items()}
+    # a call of at most 64 entries (one work item per expert) is planned inside
+    # moe_forward's gate/up launch: no plan launch to time there, so the plan
+    # is timed as moe_plan alone (its one-wavefront launch) on the last call
+    plan_in_gateup = all(st_all[k][1] == 0 for k in ("hist", "scan", "place"))
+    plan_us = us["hist"] + us["scan"] + us["place"]
+    if plan_in_gateup:
+        ids_last, w_last = chunks[-1][1], chunks[-1][2]
+        o_pl = abi.plan(ids_last, w_last, E, tm)
+
+        def plan_alone():
+            abi.moe_plan(ids_last, w_last, T, K, E, tm, o_pl["cnt"], o_pl["eoff"], o_pl["tiles"],
+                         o_pl["stok"], o_pl["sw"], o_pl["pos"], o_pl["boff"], o_pl["meta"],
+                         o_pl["scratch"])
+
+        plan_us = timed_us(plan_alone, max(args.steps, 20))
     gu_us = 1e3 * st["gateup"][0] / max(st["gateup"][1], 1)  # from the timed steps
     gu_bytes = gateup_bytes(cfg, meta, T)
     gu_s = gu_us * 1e-6
@@ -788,7 +804,12 @@ def main():
                    "weights": ("packed once into the MFMA tile layout by moe_pack_weights before "
                                "the timed steps (%.1f ms)" % pack_ms) if packed is not None
                               else "row-major [E][d][f] / [E][f][d] as generated"},
-        "plan_us": us["hist"] + us["scan"] + us["place"],
+        "plan_us": plan_us,
+        "plan_note": ("moe_forward plans this call inside its gate/up launch (at most 64 "
+                      "entries, one work item per expert); plan_us is moe_plan alone on the "
+                      "last call's routing (its one-wavefront launch), by events over "
+                      "back-to-back calls") if plan_in_gateup else
+                     "the plan's launches in moe_forward, per-kernel HIP events",
         "route_us": route_us,
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},
         "stages_note": "per-kernel HIP events in a pass after the timed steps (events around "
@@ -800,7 +821,7 @@ def main():
                        if us.get(k)},
         "gather_us": round(gather_us, 2),
         "plan_gather_combine": plan_gather_combine(
-            cfg, meta, T, us["hist"] + us["scan"] + us["place"], gather_us, us["combine"]),
+            cfg, meta, T, plan_us, gather_us, us["combine"]),
         "plan_us_by_T": plan_sizes or None,
         "plan_us_by_T_note": "moe_plan alone (one launch up to 32,768 entries), 512 experts, "
                              "top-10, tm 16, at the token counts of the page's plan table; "

@@ -180,7 +180,8 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
              int d, int f, int tm, const int32_t *eoff, const int32_t *stok, const float *sw,
              const int32_t *meta, int64_t max_rows, void *h, float *y, void *scratch,
              size_t scratch_bytes, hipStream_t s, moe_timer_t *tmr, bool have_items = false,
-             const void *x = nullptr, int T = 0, bool packed = false, int8_t *yexp = nullptr)
+             const void *x = nullptr, int T = 0, bool packed = false, int8_t *yexp = nullptr,
+             const moe::WavePlan *wp = nullptr)
 {
     const int rc = ffn_check(xs, wg, wu, wd, dtype, E, d, f, tm, eoff, stok, sw, meta, max_rows, h,
                              y, scratch, scratch_bytes);
@@ -196,7 +197,7 @@ int ffn_impl(const void *xs, const void *wg, const void *wu, const void *wd, int
         Rec r(tmr, s, MOE_STAGE_GATEUP);
         const hipError_t e =
             x ? moe::launch_gateup_gathered(z, dtype, packed, x, T, stok, wg, wu, d, f, meta,
-                                            scratch, h, s)
+                                            scratch, h, s, wp)
               : moe::launch_gateup(z, dtype, packed, xs, stok, wg, wu, d, f, meta, scratch, h, s);
         if (e != hipSuccess) return MOE_EHIP;
     }
@@ -353,10 +354,29 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     auto f32 = [&](size_t off) { return reinterpret_cast<float *>(b + off); };
     bool items = false;
     const moe::FfnShape fz = moe::ffn_shape(E, tm, z.max_rows, d, f, dtype);
-    rc = plan_impl(ids, w, T, K, E, tm, i32(L.cnt), i32(L.eoff), i32(L.tiles), i32(L.stok),
-                   f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
-                   z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items, runs_first(fz, packed));
-    if (rc != MOE_OK) return rc;
+    // The gate/up kernel gathers its rows from x itself when x is addressable
+    // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
+    const bool fused_gather = (size_t)T * d * elem_bytes(dtype) < ((size_t)1 << 31);
+    // A call of at most one wavefront of entries, one work item per expert, is
+    // planned inside the gate/up launch (moe::WavePlan): one launch fewer. Not
+    // with host weights (the cache is assigned between the plan and the
+    // GEMMs) nor with big cells (their launch precedes gate/up's).
+    moe::WavePlan wp{};
+    if (!hs && fused_gather && moe::wave_plan_fits((int64_t)T * K, tm) && !fz.big_gu &&
+        !fz.big_dn) {
+        if (!aligned(ids, 4) || !aligned(w, 4)) return MOE_EINVAL;
+        int nbits = 0;
+        while ((1 << nbits) < E) ++nbits;
+        wp = moe::WavePlan{ids, w, T * K, E, K, tm, nbits, (int)fz.max_items, (int)z.max_rows,
+                           i32(L.cnt), i32(L.eoff), i32(L.boff), i32(L.tiles), i32(L.stok),
+                           f32(L.sw), i32(L.pos), i32(L.meta)};
+        items = true;
+    } else {
+        rc = plan_impl(ids, w, T, K, E, tm, i32(L.cnt), i32(L.eoff), i32(L.tiles), i32(L.stok),
+                       f32(L.sw), i32(L.pos), i32(L.boff), i32(L.meta), b + L.plan_scratch,
+                       z.scratch_bytes, s, tmr, b + L.ffn_scratch, &items, runs_first(fz, packed));
+        if (rc != MOE_OK) return rc;
+    }
     if (hs) {
         // the routed experts' weights into the cache, the work list to slots
         if (!items) {
@@ -372,9 +392,6 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
         wu = hs->st.up;
         wd = hs->st.down;
     }
-    // The gate/up kernel gathers its rows from x itself when x is addressable
-    // by one buffer descriptor (< 2 GiB); otherwise the rows are gathered first.
-    const bool fused_gather = (size_t)T * d * elem_bytes(dtype) < ((size_t)1 << 31);
     if (!fused_gather) {
         rc = gather_impl(x, dtype, T, d, i32(L.stok), i32(L.meta), z.max_rows, b + L.xs, s, tmr);
         if (rc != MOE_OK) return rc;
@@ -388,7 +405,7 @@ int forward_impl(const void *x, const int32_t *ids, const float *w, const void *
     rc = ffn_impl(b + L.xs, wg, wu, wd, dtype, E, d, f, tm, i32(L.eoff), i32(L.stok), f32(L.sw),
                   i32(L.meta), z.max_rows, b + L.h, f32(L.y), b + L.ffn_scratch,
                   fz.scratch_bytes, s, tmr, items,
-                  fused_gather ? x : nullptr, T, packed, yexp);
+                  fused_gather ? x : nullptr, T, packed, yexp, wp.ids ? &wp : nullptr);
     if (rc != MOE_OK) return rc;
     return combine_impl(f32(L.y), z.max_rows, i32(L.pos), T, K, d, out, s, tmr, yexp);
 }

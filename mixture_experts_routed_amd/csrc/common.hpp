@@ -221,14 +221,21 @@ __device__ __forceinline__ void wave_fill_items(int n, int r0, int rows, int qbe
 // order. Give each XCD one contiguous range of the first `nlogical` logical
 // block indices (so neighbouring logical blocks share that XCD's L2), with
 // the surplus blocks of a host-sized grid at the end of each XCD's queue.
-// Returns -1 for a surplus block. gridDim.x must be a multiple of 8.
-__device__ __forceinline__ int xcd_logical_block(int nlogical)
+// Returns -1 for a surplus block. bid is the block's index among the blocks
+// that take logical blocks (blockIdx.x, or less when the grid puts other
+// blocks before them); their number must be a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block(int nlogical, int bid)
 {
-    const int xcd = blockIdx.x & 7;
-    const int local = blockIdx.x >> 3;
+    const int xcd = bid & 7;
+    const int local = bid >> 3;
     const int per = (nlogical + 7) >> 3;
     const int lb = xcd * per + local;
     return (local < per && lb < nlogical) ? lb : -1;
+}
+
+__device__ __forceinline__ int xcd_logical_block(int nlogical)
+{
+    return xcd_logical_block(nlogical, blockIdx.x);
 }
 
 }  // namespace moe

@@ -44,6 +44,7 @@
 //    turns those experts from weight streaming into matrix-core work.
 #include "common.hpp"
 #include "launch.hpp"
+#include "plan_wave.hpp"
 
 namespace moe {
 
@@ -606,13 +607,15 @@ __device__ __forceinline__ void store_cells(const GemmArgs &p, const WorkItem &i
 
 // (router weight, token) of the item's rows for the epilogue; the gate/up
 // projection has no router weight (sw is not passed) and needs the tokens only
+// (ltok != nullptr: the item's tokens from LDS, ltok[l] for its row l)
 template <bool WITH_SW>
 __device__ __forceinline__ void load_rinfo(const GemmArgs &p, const WorkItem &it, int l,
-                                           float2 *__restrict__ rinfo)
+                                           float2 *__restrict__ rinfo, const int *ltok = nullptr)
 {
     const bool ok = l < it.nrows;
     const int64_t r = it.row0 + (ok ? l : 0);
-    rinfo[l] = make_float2(WITH_SW && ok ? p.sw[r] : 0.f, __int_as_float(ok ? p.stok[r] : -1));
+    const int t = ok ? (ltok ? ltok[l] : p.stok[r]) : -1;
+    rinfo[l] = make_float2(WITH_SW && ok ? p.sw[r] : 0.f, __int_as_float(t));
 }
 
 // Launches with fewer cells than this (the GPU's workgroup slots: 2 per CU)
@@ -668,7 +671,7 @@ constexpr int kLdsU4 = 2 * tall_buf_u4(2) > 2 * kATileU4 ? 2 * tall_buf_u4(2) : 
 template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool DEEP, int NMT>
 __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it, int slice,
                                            int kb, int ke, int split, uint4 *__restrict__ a_lds,
-                                           float2 *__restrict__ rinfo)
+                                           float2 *__restrict__ rinfo, const int *ltok)
 {
     constexpr int NPL = kNpl;
     constexpr int ES = sizeof(T);
@@ -737,7 +740,7 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
         // all of x (< 2 GiB, checked by the host); a pad row (token -1) or a
         // row past the item starts at 2^31, outside the range: it reads zeros
         ra = make_rsrc(A, (uint32_t)((size_t)p.a_rows * Kd * ES));
-        const int t = arow < it.nrows ? p.stok[it.row0 + arow] : -1;
+        const int t = arow < it.nrows ? (ltok ? ltok[arow] : p.stok[it.row0 + arow]) : -1;
         va0 = (unsigned)t < (unsigned)p.a_rows ? (uint32_t)t * (uint32_t)Kd * ES : 0x80000000u;
     } else {
         ra = make_rsrc(A + (size_t)it.row0 * Kd, (uint32_t)((size_t)it.nrows * Kd * ES));
@@ -747,7 +750,7 @@ __device__ __forceinline__ void wide_cells(const GemmArgs &p, const WorkItem it,
     // made visible to all wavefronts by the barriers of the K loop (gate/up
     // needs the tokens only for its partial sums)
     if (!GATEUP || p.nsplit > 1)
-        if (tid < kItemRows) load_rinfo<!GATEUP>(p, it, tid, rinfo);
+        if (tid < kItemRows) load_rinfo<!GATEUP>(p, it, tid, rinfo, ltok);
 
     float4_t acc[NMAT][NMT][NPL];
 #pragma unroll
@@ -1084,18 +1087,43 @@ __device__ __forceinline__ void gemm_cell(const GemmArgs &p, const WorkItem *__r
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = g * kWavesPerBlock + wave;
     switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
-    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 1>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 3>(p, it, slice, kb, ke, split, lds, rinfo); break;
-    default: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, kMT>(p, it, slice, kb, ke, split, lds, rinfo); break;
+    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 1>(p, it, slice, kb, ke, split, lds, rinfo, nullptr); break;
+    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, it, slice, kb, ke, split, lds, rinfo, nullptr); break;
+    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 3>(p, it, slice, kb, ke, split, lds, rinfo, nullptr); break;
+    default: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, kMT>(p, it, slice, kb, ke, split, lds, rinfo, nullptr); break;
+    }
+}
+
+// A single item's wide cell, its token rows from LDS (ltok[r] for row r).
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool DEEP>
+__device__ __forceinline__ void single_cell(const GemmArgs &p, const WorkItem it, int g, int kb,
+                                            int ke, int split, uint4 *__restrict__ lds,
+                                            float2 *__restrict__ rinfo, const int *ltok)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slice = g * kWavesPerBlock + wave;
+    switch ((it.nrows + 15) >> 4) {  // m-tiles of this item (uniform per workgroup)
+    case 1: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 1>(p, it, slice, kb, ke, split, lds, rinfo, ltok); break;
+    case 2: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 2>(p, it, slice, kb, ke, split, lds, rinfo, ltok); break;
+    case 3: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, 3>(p, it, slice, kb, ke, split, lds, rinfo, ltok); break;
+    default: wide_cells<T, GATEUP, GATHERED, PACKED, DEEP, kMT>(p, it, slice, kb, ke, split, lds, rinfo, ltok); break;
     }
 }
 
 // One workgroup per (work item, group of 4 column slices, K split).
-template <typename T, bool GATEUP, bool GATHERED, bool PACKED>
+// WP (gathered gate/up of a call planned here, WavePlan wp): workgroup 0
+// writes the plan and the work list for the later kernels (plan_wave_body,
+// one wavefront, LDS borrowed from the tiles), workgroups 1-7 have nothing
+// to do, and workgroup 8 + b finds the item of its logical block b from the
+// ids (wave_plan_item: every item is single, so there are no runs and no list
+// to read) and keeps the item's tokens in LDS for its A-operand rows. A
+// template instance of its own, so that the other launches' code is
+// untouched.
+template <typename T, bool GATEUP, bool GATHERED, bool PACKED, bool WP = false>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
                                                         const int32_t *__restrict__ ctl,
-                                                        const WorkItem *__restrict__ items)
+                                                        const WorkItem *__restrict__ items,
+                                                        const WavePlan wp)
 {
     __shared__ uint4 lds[kLdsU4];
     __shared__ float2 rinfo[kWavesPerBlock * kItemRows];
@@ -1103,26 +1131,67 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(const GemmArgs p,
     constexpr int KSTEP = 4 * Elt<T>::KR;
     const int gs = (p.N + 4 * SW - 1) / (4 * SW);       // column groups per item
     const int per_item = gs * p.nsplit;
-    const int nitems = ctl[0];
-    const int ifirst = p.skip_quads ? min(ctl[1], nitems) : 0;
-    const int lb = xcd_logical_block((nitems - ifirst) * per_item);
-    if (lb < 0) return;  // whole workgroup: no barrier reached
-    const int il = lb / per_item;  // item ifirst + il
-    const int i = ifirst + il;
-    const int rem = lb - il * per_item;
-    const int g = rem / p.nsplit, split = rem - g * p.nsplit;
-    const int kb = split * p.split_steps * KSTEP;
-    const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
-    const WorkItem it = items[i];
-    // weight-stream depth of the launch: deep when at least half the items are
-    // in runs or when the cells do not fill the GPU's workgroup slots, else
-    // shallow (the same for every workgroup)
-    if (2 * ctl[2] >= nitems || (nitems - ifirst) * per_item < kDeepBelowCells)
-        gemm_cell<T, GATEUP, GATHERED, PACKED, true>(p, items, it, i, nitems, g, kb, ke, split, lds,
-                                                     rinfo);
-    else
-        gemm_cell<T, GATEUP, GATHERED, PACKED, false>(p, items, it, i, nitems, g, kb, ke, split,
-                                                      lds, rinfo);
+    if constexpr (WP) {
+        static_assert(GATEUP && GATHERED, "planned here: the gathered gate/up launch only");
+        static_assert(2 * kMaxExperts * 4 <= kLdsU4 * 16, "plan counters fit the tile LDS");
+        __shared__ int s_tok[kItemRows];
+        __shared__ WorkItem s_item;
+        __shared__ int s_nb[2];
+        if (blockIdx.x < 8) {
+            if (blockIdx.x == 0 && threadIdx.x < kWave) {
+                int *ls = reinterpret_cast<int *>(lds);
+                plan_wave_body(wp.ids, wp.w, wp.nent, wp.E, wp.K, wp.tm, wp.nbits, wp.cnt,
+                               wp.eoff, wp.boff, wp.tiles, wp.stok, wp.sw, wp.pos, wp.meta,
+                               const_cast<int32_t *>(ctl), const_cast<WorkItem *>(items),
+                               wp.max_items, wp.max_rows, 0, ls, ls + kMaxExperts);
+            }
+            return;  // (no barrier in these workgroups)
+        }
+        if (threadIdx.x < kWave) {
+            int n, b;
+            WorkItem w_it;
+            wave_plan_item(wp.ids, wp.nent, wp.E, wp.K, wp.tm, wp.nbits, wp.max_rows, per_item,
+                           blockIdx.x - 8, &n, &b, &w_it, s_tok);
+            if (threadIdx.x == 0) {
+                s_nb[0] = n;
+                s_nb[1] = b;
+                s_item = w_it;
+            }
+        }
+        __syncthreads();
+        const int nitems = s_nb[0], lb = s_nb[1];
+        if (lb < 0) return;  // whole workgroup, after its only barrier outside the cell
+        const WorkItem it = s_item;
+        const int rem = lb - (lb / per_item) * per_item;
+        const int g = rem / p.nsplit, split = rem - g * p.nsplit;
+        const int kb = split * p.split_steps * KSTEP;
+        const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
+        if (nitems * per_item < kDeepBelowCells)  // (no runs)
+            single_cell<T, true, true, PACKED, true>(p, it, g, kb, ke, split, lds, rinfo, s_tok);
+        else
+            single_cell<T, true, true, PACKED, false>(p, it, g, kb, ke, split, lds, rinfo, s_tok);
+    } else {
+        const int nitems = ctl[0];
+        const int ifirst = p.skip_quads ? min(ctl[1], nitems) : 0;
+        const int lb = xcd_logical_block((nitems - ifirst) * per_item);
+        if (lb < 0) return;  // whole workgroup: no barrier reached
+        const int il = lb / per_item;  // item ifirst + il
+        const int i = ifirst + il;
+        const int rem = lb - il * per_item;
+        const int g = rem / p.nsplit, split = rem - g * p.nsplit;
+        const int kb = split * p.split_steps * KSTEP;
+        const int ke = min(p.Kd, kb + p.split_steps * KSTEP);
+        const WorkItem it = items[i];
+        // weight-stream depth of the launch: deep when at least half the items
+        // are in runs or when the cells do not fill the GPU's workgroup slots,
+        // else shallow (the same for every workgroup)
+        if (2 * ctl[2] >= nitems || (nitems - ifirst) * per_item < kDeepBelowCells)
+            gemm_cell<T, GATEUP, GATHERED, PACKED, true>(p, items, it, i, nitems, g, kb, ke, split,
+                                                         lds, rinfo);
+        else
+            gemm_cell<T, GATEUP, GATHERED, PACKED, false>(p, items, it, i, nitems, g, kb, ke,
+                                                          split, lds, rinfo);
+    }
 }
 
 // ---- big cells: runs of 4 items on 8 wavefronts (packed, 16-bit) ------------
@@ -1596,7 +1665,8 @@ unsigned reduce_blocks(int64_t rows, int N) { return (unsigned)((rows * (N / 4) 
 template <typename T, bool PACKED>
 hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
                     const int32_t *stok, const void *wg, const void *wu, int d, int f,
-                    const int32_t *meta, const void *scratch, void *h, hipStream_t s)
+                    const int32_t *meta, const void *scratch, void *h, hipStream_t s,
+                    const WavePlan *wp)
 {
     GemmArgs p = gemm_args(z, scratch, true);
     p.A = a;
@@ -1620,12 +1690,16 @@ hipError_t gateup_t(const FfnShape &z, const void *a, int a_rows, bool gathered,
                                    ctl_of(scratch), items_of(scratch));
         }
     }
-    if (gathered)  // rows gathered from x through stok
+    const WavePlan none{};
+    if (gathered && wp && wp->ids)  // planned here: 8 workgroups before the cells'
+        hipLaunchKernelGGL((k_expert_gemm<T, true, true, PACKED, true>), dim3(grid.x + 8),
+                           dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch), *wp);
+    else if (gathered)  // rows gathered from x through stok
         hipLaunchKernelGGL((k_expert_gemm<T, true, true, PACKED>), grid, dim3(256), 0, s, p,
-                           ctl_of(scratch), items_of(scratch));
+                           ctl_of(scratch), items_of(scratch), none);
     else
         hipLaunchKernelGGL((k_expert_gemm<T, true, false, PACKED>), grid, dim3(256), 0, s, p,
-                           ctl_of(scratch), items_of(scratch));
+                           ctl_of(scratch), items_of(scratch), none);
     if (z.split_gu > 1) {
         const hipError_t e = reduce_gateup<T>(p.nsplit, dim3(reduce_blocks(z.max_rows, f)), s,
                                               p.part, p.plane, f, stok, meta, z.max_rows,
@@ -1662,7 +1736,7 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
         }
     }
     hipLaunchKernelGGL((k_expert_gemm<T, false, false, PACKED>), dim3((unsigned)z.blocks_dn),
-                       dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch));
+                       dim3(256), 0, s, p, ctl_of(scratch), items_of(scratch), WavePlan{});
     if (z.split_dn > 1) {
         const hipError_t e =
             p.yexp ? reduce_down_y16(p.nsplit,
@@ -1679,11 +1753,13 @@ hipError_t down_t(const FfnShape &z, const void *h, const void *wd, int d, int f
 template <typename T>
 hipError_t gateup_any(const FfnShape &z, bool packed, const void *a, int a_rows, bool gathered,
                       const int32_t *stok, const void *wg, const void *wu, int d, int f,
-                      const int32_t *meta, const void *scratch, void *h, hipStream_t s)
+                      const int32_t *meta, const void *scratch, void *h, hipStream_t s,
+                      const WavePlan *wp = nullptr)
 {
-    return packed ? gateup_t<T, true>(z, a, a_rows, gathered, stok, wg, wu, d, f, meta, scratch, h, s)
+    return packed ? gateup_t<T, true>(z, a, a_rows, gathered, stok, wg, wu, d, f, meta, scratch, h,
+                                      s, wp)
                   : gateup_t<T, false>(z, a, a_rows, gathered, stok, wg, wu, d, f, meta, scratch, h,
-                                       s);
+                                       s, wp);
 }
 
 }  // namespace
@@ -1701,14 +1777,21 @@ hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *
 
 hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
-                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s)
+                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s,
+                                  const WavePlan *wp)
 {
     if (dtype == 1)
-        return gateup_any<_Float16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+        return gateup_any<_Float16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s,
+                                    wp);
     if (dtype == 2)
-        return gateup_any<__bf16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
-    return gateup_any<float>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s);
+        return gateup_any<__bf16>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s,
+                                  wp);
+    return gateup_any<float>(z, packed, x, T, true, stok, wg, wu, d, f, meta, scratch, h, s, wp);
 }
+
+// every expert of a call of at most 64 entries pads to at most 64 rows (one
+// work item) when tm divides 64
+bool wave_plan_fits(int64_t nent, int tm) { return nent <= kWave && tm >= 1 && kWave % tm == 0; }
 
 hipError_t launch_down(const FfnShape &z, int dtype, bool packed, const void *h, const void *wd,
                        int d, int f, const int32_t *stok, const float *sw, const int32_t *meta,

@@ -64,6 +64,22 @@ struct FfnShape {
 };
 FfnShape ffn_shape(int E, int tm, int64_t max_rows, int d, int f, int dtype);
 
+// A call of at most one wavefront of entries whose experts each get one work
+// item (wave_plan_fits) can be planned inside the gathered gate/up launch:
+// every workgroup finds its own work item from the ids, and the launch's first
+// workgroup writes the plan's outputs and the work list for the kernels after
+// it, as the one-wavefront plan launch would (bit for bit). ids == nullptr:
+// the launch reads the work list the plan wrote.
+struct WavePlan {
+    const int32_t *ids;
+    const float *w;
+    int nent, E, K, tm, nbits, max_items, max_rows;
+    int32_t *cnt, *eoff, *boff, *tiles, *stok;
+    float *sw;
+    int32_t *pos, *meta;
+};
+bool wave_plan_fits(int64_t nent, int tm);
+
 // runs_first: the items in runs of 4 first (item_slot), for the big cells
 hipError_t launch_worklist(const int32_t *eoff, int E, int64_t max_rows, void *scratch,
                            int64_t max_items, bool runs_first, hipStream_t s);
@@ -72,9 +88,11 @@ hipError_t launch_gateup(const FfnShape &z, int dtype, bool packed, const void *
                          const int32_t *meta, const void *scratch, void *h, hipStream_t s);
 // gate/up reading row r straight from x[stok[r]] (the gather fused into the
 // A-tile loads); x must be smaller than 2 GiB.
+// wp != nullptr with wp->ids set: the call is planned inside this launch (WavePlan).
 hipError_t launch_gateup_gathered(const FfnShape &z, int dtype, bool packed, const void *x, int T,
                                   const int32_t *stok, const void *wg, const void *wu, int d, int f,
-                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s);
+                                  const int32_t *meta, const void *scratch, void *h, hipStream_t s,
+                                  const WavePlan *wp = nullptr);
 // yexp == nullptr: y is fp32 [rows][d]; otherwise (16-bit types only) y holds
 // binary16 rows and yexp [rows][ceil(d / 128)] their block exponents (the
 // compact format of common.hpp)

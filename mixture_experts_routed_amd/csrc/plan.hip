@@ -18,6 +18,7 @@
 // relies on top-10 routing to bound the count per sub-block.
 #include "common.hpp"
 #include "launch.hpp"
+#include "plan_wave.hpp"
 
 namespace moe {
 
@@ -401,14 +402,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan_fused(
 
 // Plan of at most one wavefront of entries (decode-sized calls): the outputs
 // of k_plan_fused (with one block) from a single 64-lane workgroup, so that no
-// barrier is needed and the launch has one wavefront to start. Lane l holds
-// entry l and experts [l * epl, (l + 1) * epl), epl = ceil(E / 64) <= 16: the
-// ranks come from the same ballots as k_place; the leader of each expert's
-// lanes writes its count to LDS; each lane then takes its experts' counts in
-// order (a running sum plus a wavefront scan for the padded-row offsets and
-// the work-list slots) and writes their outputs.
-constexpr int kWaveExperts = kMaxExperts / kWave;
-
+// barrier is needed and the launch has one wavefront to start
+// (plan_wave_body).
 __global__ __launch_bounds__(kWave) void k_plan_wave(
     const int32_t *__restrict__ ids, const float *__restrict__ w, int nent, int E, int K, int tm,
     int nbits, int32_t *__restrict__ cnt, int32_t *__restrict__ eoff, int32_t *__restrict__ boff,
@@ -417,106 +412,8 @@ __global__ __launch_bounds__(kWave) void k_plan_wave(
     WorkItem *__restrict__ items, int max_items, int max_rows, int runs_first)
 {
     __shared__ int s_cnt[kMaxExperts], s_eoff[kMaxExperts];
-    const int lane = threadIdx.x;
-    const bool inb = lane < nent;
-    const int e = inb ? ids[lane] : -1;
-    const float wi = inb ? w[lane] : 0.0f;
-    const int epl = (E + kWave - 1) / kWave;
-    const int e0 = lane * epl;
-#pragma unroll
-    for (int j = 0; j < kWaveExperts; ++j)
-        if (j < epl && e0 + j < E) s_cnt[e0 + j] = 0;
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int p = 0; p < nbits; ++p) {
-        const bool bit = (e >> p) & 1;
-        const uint64_t bl = __ballot(bit);
-        same &= bit ? bl : ~bl;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(same & below);
-    const int nskip = __popcll(__ballot(inb && e == -1));
-    const int nbad = __popcll(__ballot(inb && e != -1 && !valid));
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // the counters cleared (lgkmcnt(0))
-    if (valid && rank == 0) s_cnt[e] = __popcll(same);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-
-    // this lane's experts: counts, padded rows and items, then the offsets
-    int c[kWaveExperts];
-    int lrows = 0, lq = 0, lr = 0, lp = 0, lact = 0, lmax = 0;
-#pragma unroll
-    for (int j = 0; j < kWaveExperts; ++j) {
-        c[j] = (j < epl && e0 + j < E) ? s_cnt[e0 + j] : 0;
-        const int rows = (c[j] + tm - 1) / tm * tm;
-        const int nit = (rows + kItemRows - 1) / kItemRows, nit4 = nit & ~3;
-        lrows += rows;
-        lq += nit4;
-        lr += nit - nit4;
-        lp += nit - nit4 >= 2 ? 2 : 0;
-        lact += c[j] > 0 ? 1 : 0;
-        lmax = max(lmax, c[j]);
-    }
-    const int srow = wave_inclusive_scan(lrows, lane);
-    const int sq = wave_inclusive_scan(lq, lane);
-    const int sr = wave_inclusive_scan(lr, lane);
-    const int total = __builtin_amdgcn_readlane(srow, kWave - 1);
-    const int qtotal = __builtin_amdgcn_readlane(sq, kWave - 1);
-    const int rtotal = __builtin_amdgcn_readlane(sr, kWave - 1);
-    const int ptotal = wave_sum(lp), nact = wave_sum(lact), maxc = wave_max(lmax);
-    int start = srow - lrows, qb = sq - lq, rb = sr - lr;
-#pragma unroll
-    for (int j = 0; j < kWaveExperts; ++j) {
-        const int ex = e0 + j;
-        if (!(j < epl && ex < E)) continue;
-        const int rows = (c[j] + tm - 1) / tm * tm;
-        const int nit = (rows + kItemRows - 1) / kItemRows, nit4 = nit & ~3;
-        s_eoff[ex] = start;
-        cnt[ex] = c[j];
-        eoff[ex] = start;
-        boff[ex] = 0;  // one block: no entries before it
-        for (int t = 0; t < rows / tm; ++t) tiles[start / tm + t] = ex;
-        for (int r = start + c[j]; r < start + rows; ++r) {  // pad rows
-            stok[r] = -1;
-            sw[r] = 0.0f;
-        }
-        if (items)
-            for (int q = 0; q < nit; ++q)
-                put_item(q, nit, start, rows, qb, rb, qtotal, runs_first != 0, ex, max_items,
-                         max_rows, items);
-        start += rows;
-        qb += nit4;
-        rb += nit - nit4;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // s_eoff written
-
-    // placement: the expert's offset plus the rank among its lanes
-    if (valid) {
-        const int row = s_eoff[e] + rank;
-        pos[lane] = row;
-        stok[row] = lane / K;
-        sw[row] = wi;
-    } else if (inb) {
-        pos[lane] = -1;
-    }
-    if (lane == 0) {
-        eoff[E] = total;
-        meta[kMetaNent] = nent;
-        meta[kMetaNblk] = 1;
-        meta[kMetaNr] = total;
-        meta[kMetaNt] = total / tm;
-        meta[kMetaNactive] = nact;
-        meta[kMetaMaxcnt] = maxc;
-        meta[kMetaNskip] = nskip;
-        meta[kMetaNbad] = nbad;
-        meta[kMetaTm] = tm;
-        meta[kMetaE] = E;
-        meta[kMetaK] = K;
-        if (items) {
-            ctl[0] = min(qtotal + rtotal, max_items);
-            ctl[1] = runs_first ? min(qtotal, max_items) & ~3 : 0;
-            ctl[2] = min(qtotal + ptotal, max_items);
-        }
-    }
+    plan_wave_body(ids, w, nent, E, K, tm, nbits, cnt, eoff, boff, tiles, stok, sw, pos, meta, ctl,
+                   items, max_items, max_rows, runs_first, s_cnt, s_eoff);
 }
 
 int plan_fused_max_blocks() { return kFusedMaxBlocks; }
