@@ -267,6 +267,28 @@ def timed_us(fn, n):
     return a.elapsed_time(b) * 1e3 / n
 
 
+def queued_us(fn, n, dev):
+    """mean microseconds per call of fn() over n back-to-back calls enqueued
+    while the GPU is still busy with a 4 GiB fill, so that the calls run back
+    to back on the GPU however long the host takes to issue each one (for
+    launches shorter than the host's per-call cost); torch events on the
+    current stream"""
+    import torch
+
+    for _ in range(3):
+        fn()
+    busy = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy.fill_(0)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    del busy
+    return a.elapsed_time(b) * 1e3 / n
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -714,7 +736,7 @@ def main():
                 abi.moe_plan(pid, pw, Tp, K, E, tm, o["cnt"], o["eoff"], o["tiles"], o["stok"],
                              o["sw"], o["pos"], o["boff"], o["meta"], o["scratch"])
 
-            us_p = timed_us(plan_call, max(args.steps, 20))
+            us_p = queued_us(plan_call, 40, dev)
             plan_sizes[str(Tp)] = {"us": round(us_p, 2),
                                    "padded_rows": int(o["meta"][2].item()),
                                    "nblk": int(o["meta"][1].item())}
@@ -753,7 +775,7 @@ def main():
                          o_pl["stok"], o_pl["sw"], o_pl["pos"], o_pl["boff"], o_pl["meta"],
                          o_pl["scratch"])
 
-        plan_us = timed_us(plan_alone, max(args.steps, 20))
+        plan_us = queued_us(plan_alone, 40, dev)
     gu_us = 1e3 * st["gateup"][0] / max(st["gateup"][1], 1)  # from the timed steps
     gu_bytes = gateup_bytes(cfg, meta, T)
     gu_s = gu_us * 1e-6
@@ -807,8 +829,8 @@ def main():
         "plan_us": plan_us,
         "plan_note": ("moe_forward plans this call inside its gate/up launch (at most 64 "
                       "entries, one work item per expert); plan_us is moe_plan alone on the "
-                      "last call's routing (its one-wavefront launch), by events over "
-                      "back-to-back calls") if plan_in_gateup else
+                      "last call's routing (its one-wavefront launch), 40 calls queued back to "
+                      "back behind a 4 GiB fill, by events") if plan_in_gateup else
                      "the plan's launches in moe_forward, per-kernel HIP events",
         "route_us": route_us,
         "stages_us": {k: round(v, 2) for k, v in us.items() if st_all[k][1] > 0},
@@ -824,7 +846,8 @@ def main():
             cfg, meta, T, plan_us, gather_us, us["combine"]),
         "plan_us_by_T": plan_sizes or None,
         "plan_us_by_T_note": "moe_plan alone (one launch up to 32,768 entries), 512 experts, "
-                             "top-10, tm 16, at the token counts of the page's plan table; "
+                             "top-10, tm 16, at the token counts of the page's plan table, 40 "
+                             "calls queued back to back behind a 4 GiB fill, by events; "
                              "padded_rows is the plan's nr",
         "rowmajor": rowmajor,
         "step_us": step_us,
