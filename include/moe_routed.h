@@ -301,9 +301,12 @@ int moe_forward_workspace(int T, int K, int E, int d, int f, int tm, int dtype, 
  * moe_forward -- one routed MoE layer: the results of moe_plan, moe_gather,
  * moe_expert_ffn and moe_combine in sequence on one stream, intermediates in
  * `workspace`. Fewer launches than calling them one by one: for T*K <= 32768
- * the plan is one kernel that also writes the FFN's work list, and when x is
- * smaller than 2 GiB the gate/up kernel reads its rows from x through stok
- * (the gather is fused; the workspace's xs rows are then left unwritten).
+ * the plan is one kernel that also writes the FFN's work list; for T*K <= 64
+ * with tm dividing 64 (and x below 2 GiB) that plan runs inside the gate/up
+ * kernel, whose workgroups find their work items from the ids themselves (the
+ * workspace's plan arrays get the same values); and when x is smaller than 2
+ * GiB the gate/up kernel reads its rows from x through stok (the gather is
+ * fused; the workspace's xs rows are then left unwritten).
  * For fp16 and bf16 layers the expert outputs y are kept in a compact format,
  * half the bytes of fp32 rows: each row is cut into blocks of 128 columns, a
  * block holds binary16 values s and one exponent e (int8) and stands for
