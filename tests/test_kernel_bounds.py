@@ -311,3 +311,49 @@ def test_gather_partition_copies_every_row_once_in_bounds(cfg):
             assert np.all((tt < T))  # tokens read are rows of x (pads read nothing)
             copies[mine] += 1
     assert np.all(copies == 1)
+
+
+def wave_item_model(ids, E, K, tm, max_rows):
+    """The gate/up launch's own work items for a call of at most 64 entries
+    (wave_plan_item, lane l = entry l): an entry is its expert's first when no
+    earlier entry has its id; item j is the j-th such expert by id, its rows
+    start after the padded rows of the experts below it; its row r holds the
+    token of the expert's r-th entry. Returns items [n, 4] and the tokens."""
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    valid = [0 <= e < E for e in flat]
+    count = {}
+    for e, v in zip(flat, valid):
+        if v:
+            count[e] = count.get(e, 0) + 1
+    firsts = sorted(count)
+    rows = {e: ceil(count[e], tm) * tm for e in firsts}
+    items, toks = [], []
+    for e in firsts:
+        below = sum(rows[x] for x in firsts if x < e)
+        items.append((e, below, min(ITEM, rows[e], max_rows - below), 1))
+        t = [l // K for l, (x, v) in enumerate(zip(flat, valid)) if v and x == e]
+        toks.append(t + [-1] * (ITEM - len(t)))
+    return np.array(items, np.int32).reshape(-1, 4), toks
+
+
+WAVE_CASES = [(4, 8, 128, 16, 0.0, 0.0, 1), (1, 1, 1, 16, 0.0, 0.0, 2),
+              (8, 8, 1024, 16, 0.1, 0.05, 3), (16, 4, 4, 1, 0.0, 0.0, 4),
+              (2, 32, 100, 64, 0.5, 0.0, 5), (64, 1, 1, 64, 0.0, 0.0, 6),
+              (3, 16, 16, 8, 0.2, 0.2, 7), (5, 2, 8, 32, 1.0, 0.0, 8), (32, 2, 3, 2, 0.0, 0.3, 9)]
+
+
+@pytest.mark.parametrize("T,K,E,tm,ps,pb,seed", WAVE_CASES)
+def test_in_launch_items_are_the_work_list(T, K, E, tm, ps, pb, seed):
+    """the items the gate/up launch derives itself (calls of at most 64 entries,
+    tm dividing 64) are the documented work list of the oracle's plan, one single
+    item per routed expert, and their token rows are the plan's stok"""
+    assert T * K <= 64 and 64 % tm == 0
+    ids = synth.random_ids(seed, T, K, E, p_skip=ps, p_bad=pb)
+    w = synth.random_rows(seed, T, K)
+    R = abi.moe_plan_sizes(T, K, E, tm).max_rows
+    p = oracle.plan(ids, w, E, tm)
+    want, _, runs = worklist_model(p["eoff"], E, R, runs_first=False)
+    got, toks = wave_item_model(ids, E, K, tm, R)
+    assert runs == 0 and np.array_equal(got, want)
+    for (e, r0, nr, _), t in zip(got, toks):
+        assert list(p["stok"][r0:r0 + nr]) == t[:nr]
